@@ -1,0 +1,122 @@
+// Device-side building blocks shared by the pgemm kernels (gfx950 only).
+//
+//  * vector types for the v_mfma_f32_32x32x16_{f16,bf16} operands;
+//  * buffer resources and direct-to-LDS 16-byte loads
+//    (buffer_load_dwordx4 ... lds), whose out-of-range lanes read zero;
+//  * the LDS ring: S slots, each an A tile [BM][BK] followed by a B tile
+//    [BN][BK], stored as 16-byte granules with an XOR swizzle;
+//  * the workgroup -> output-tile map (XCD-aware, grouped);
+//  * credit counters in LDS (wait / trigger).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pgemm {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kWave = 64;
+
+// Buffer resource word 3 for raw (unswizzled, untyped) buffers on gfx9 parts.
+constexpr int kRsrcWord3 = 0x00020000;
+// Any byte offset at or above the resource's size reads as zero; this one is
+// used for lanes whose chunk lies past K.  Resource sizes stay below it.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+// One wave-wide direct-to-LDS load: lane l copies 16 bytes from
+// rsrc + voffset(l) to lds_dst + 16 * l.  `lds_dst` must be wave-uniform.
+__device__ __forceinline__ void load_lds_x4(__amdgpu_buffer_rsrc_t rsrc, char *lds_dst, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds_dst, 16, voffset, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// ----------------------------------------------------------------- ring ---
+//
+// A ring slot holds the A tile (rows of lhs) and then the B tile (rows of
+// rhs), both K-contiguous.  A row of BK halves is CPR = BK/8 granules of 16
+// bytes.  Logical chunk c of row r is stored at position c ^ swz(r), where
+// swz(r) = (r / (16 / CPR)) mod CPR.  With that choice any 16 consecutive
+// rows read at the same chunk touch 16 different granules of a 256-byte
+// window, so the fragment reads (lane l reads row base + l%32) are free of
+// bank conflicts; the direct-to-LDS writes fill 1 KiB contiguously per
+// instruction and never conflict.
+template <int BK>
+struct RingRow {
+  static constexpr int CPR = BK / 8;              // granules per row
+  static constexpr int ROW_BYTES = BK * 2;
+  static constexpr int ROWS_PER_WINDOW = 16 / CPR; // rows per 256 bytes
+  static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+  __device__ __forceinline__ static int swz(int r) { return (r / ROWS_PER_WINDOW) % CPR; }
+};
+
+// Output tile for a workgroup.  Workgroups are dispatched round-robin over
+// the 8 XCDs, each with its own L2: ids are first regrouped so that every XCD
+// receives a contiguous run, then runs are walked in groups of `group_m`
+// row panels so that concurrently resident tiles share A and B panels.
+__device__ __forceinline__ void tile_of_block(int64_t bid, int64_t nblocks, int tiles_m, int tiles_n,
+                                              int group_m, int *bm, int *bn) {
+  constexpr int kXcds = 8;
+  int64_t per = nblocks / kXcds;
+  int64_t id = bid;
+  if (bid < per * kXcds) id = (bid % kXcds) * per + bid / kXcds;
+  int64_t span = (int64_t)group_m * tiles_n;
+  int64_t g = id / span;
+  int64_t first = g * group_m;
+  int64_t gsize = tiles_m - first < group_m ? tiles_m - first : group_m;
+  int64_t in = id % span;
+  *bm = (int)(first + in % gsize);
+  *bn = (int)(in / gsize);
+}
+
+// -------------------------------------------------------------- credits ---
+//
+// Monotonic LDS counters.  trigger adds one; a waiter for round r of a slot
+// waits until the counter reaches (r + 1) * (number of triggering waves).
+// A wait polls with s_sleep between reads and gives up after `max_polls`
+// reads, recording the failure in *err (so a protocol error can never hang
+// the device).
+__device__ __forceinline__ uint32_t lds_load_relaxed(uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void credit_trigger(uint32_t *ctr) {
+  compiler_fence();
+  if ((threadIdx.x & (kWave - 1)) == 0)
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  compiler_fence();
+}
+
+__device__ __forceinline__ void credit_wait(uint32_t *ctr, uint32_t target, uint32_t max_polls,
+                                            uint32_t *err) {
+  uint32_t polls = 0;
+  while (lds_load_relaxed(ctr) < target) {
+    if (++polls > max_polls) {
+      if ((threadIdx.x & (kWave - 1)) == 0) atomicOr(err, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  compiler_fence();
+}
+
+}  // namespace pgemm

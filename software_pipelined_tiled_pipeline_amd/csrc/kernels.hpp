@@ -1,0 +1,307 @@
+// The pgemm kernels.
+//
+//  s32_nn_kernel  int32 NN, one output per thread, VALU multiply-add,
+//                 prologue / steady / epilogue over a two-slot ring whose
+//                 slot roles are swapped after every tile.
+//  nt_swap_kernel f16/bf16 NT, one schedule for all waves: every wave issues
+//                 direct-to-LDS loads for tile t+S-1 and runs MFMA on tile t,
+//                 one workgroup barrier per tile.
+//  nt_ws_kernel   f16/bf16 NT, producer waves and consumer waves coordinated
+//                 by per-slot full/empty credit counters in LDS.
+//
+// Pipelining follows Croqtile ch.6 ("Synchronization: pipelines, events and
+// double buffering") and the modulo schedule of the TileLang chapter
+// "pipeline-sync-multibuffer" (section 2.3: prologue, rolled steady body,
+// epilogue; section 2.4: a buffer written in stage 0 and read S-1 stages
+// later needs S versions).
+#pragma once
+
+#include "wave_mma.hpp"
+
+namespace pgemm {
+
+// ================================================================ int32 NN
+
+// Thread (qx, qy) of workgroup (px, py) owns out[16 px + qx][16 py + qy];
+// tile t of lhs is rows 16 px.., columns 16 t..; tile t of rhs is rows
+// 16 t.., columns 16 py...  Elements outside the matrices load as zero.
+template <int S>
+__global__ void __launch_bounds__(256) s32_nn_kernel(const int32_t *__restrict__ lhs,
+                                                     const int32_t *__restrict__ rhs,
+                                                     int32_t *__restrict__ out, int M, int N, int K) {
+  constexpr int T = 16;
+  __shared__ int32_t lhs_s[S][T][T];
+  __shared__ int32_t rhs_s[S][T][T];
+  const int px = blockIdx.x, py = blockIdx.y;
+  const int qx = threadIdx.x / T, qy = threadIdx.x % T;
+  const int gm = px * T + qx, gn = py * T + qy;
+  const int n_k = (K + T - 1) / T;
+
+  int32_t a_reg = 0, b_reg = 0;
+  auto fetch = [&](int t) {  // global -> registers
+    const int ka = t * T + qy, kb = t * T + qx;
+    a_reg = (gm < M && ka < K) ? lhs[(int64_t)gm * K + ka] : 0;
+    b_reg = (kb < K && gn < N) ? rhs[(int64_t)kb * N + gn] : 0;
+  };
+  auto put = [&](int slot) {  // registers -> LDS slot
+    lhs_s[slot][qx][qy] = a_reg;
+    rhs_s[slot][qx][qy] = b_reg;
+  };
+  uint32_t acc = 0;  // wraps modulo 2^32
+  auto mac = [&](int slot) {
+#pragma unroll
+    for (int k = 0; k < T; ++k) acc += (uint32_t)lhs_s[slot][qx][k] * (uint32_t)rhs_s[slot][k][qy];
+  };
+
+  if constexpr (S == 1) {
+    for (int t = 0; t < n_k; ++t) {
+      fetch(t);
+      put(0);
+      __syncthreads();
+      mac(0);
+      __syncthreads();
+    }
+  } else {
+    if (n_k > 0) {
+      int cur = 0, nxt = 1;
+      fetch(0);  // prologue: tile 0 into the current slot
+      put(cur);
+      __syncthreads();
+      for (int t = 1; t < n_k; ++t) {  // steady state
+        fetch(t);                      // loads of tile t in flight ...
+        mac(cur);                      // ... while tile t-1 is consumed
+        put(nxt);
+        __syncthreads();
+        const int tmp = cur;  // swap the slot names, not the bytes
+        cur = nxt;
+        nxt = tmp;
+      }
+      mac(cur);  // epilogue: drain the last tile
+    }
+  }
+  if (gm < M && gn < N) out[(int64_t)gm * N + gn] = (int32_t)acc;
+}
+
+// ============================================================== NT common
+
+// Direct-to-LDS fill of one ring slot.  The slot's INSTR wave-instructions
+// (64 granules each: first the A tile rows, then the B tile rows) are split
+// over the loading waves; this wave issues instructions first .. first+count-1.
+// Granule g of a tile is row g / CPR, position g % CPR, which holds logical
+// chunk (g % CPR) ^ swz(row): the global source is chosen to match.  Rows past
+// the matrix edge fall outside the buffer resource and read zero; chunks past
+// K are sent to an out-of-range offset (K is a multiple of 8, so a chunk is
+// either wholly inside or wholly outside).
+template <int BM, int BN, int BK>
+struct SlotLoader {
+  using Row = RingRow<BK>;
+  static constexpr int CPR = Row::CPR;
+  static constexpr int A_INSTR = BM * CPR / kWave;
+  static constexpr int INSTR = (BM + BN) * CPR / kWave;
+  static constexpr int SLOT_BYTES = (BM + BN) * Row::ROW_BYTES;
+  static_assert((BM * CPR) % kWave == 0 && (BN * CPR) % kWave == 0, "tiles fill whole instructions");
+
+  __amdgpu_buffer_rsrc_t ra, rb;
+  int K;
+
+  __device__ __forceinline__ void init(const uint16_t *lhs, const uint16_t *rhs, int M, int N, int K_,
+                                       int m0, int n0) {
+    K = K_;
+    const int rows_a = M - m0 < BM ? M - m0 : BM;
+    const int rows_b = N - n0 < BN ? N - n0 : BN;
+    ra = make_rsrc(lhs + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K * 2u);
+    rb = make_rsrc(rhs + (int64_t)n0 * K, (uint32_t)rows_b * (uint32_t)K * 2u);
+  }
+
+  template <int COUNT>
+  __device__ __forceinline__ void load(char *slot, int t, int first, int lane) const {
+    const int k0 = t * BK;
+    const bool whole = k0 + BK <= K;
+#pragma unroll
+    for (int i = 0; i < COUNT; ++i) {
+      const int j = first + i;  // wave-uniform
+      const bool is_a = j < A_INSTR;
+      const int jj = is_a ? j : j - A_INSTR;
+      const int row = jj * (kWave / CPR) + lane / CPR;
+      const int chunk = (lane % CPR) ^ Row::swz(row);
+      const int kc = k0 + chunk * 8;
+      uint32_t off = ((uint32_t)row * (uint32_t)K + (uint32_t)kc) * 2u;
+      if (!whole && kc >= K) off = kOobOffset;
+      load_lds_x4(is_a ? ra : rb, slot + j * (kWave * 16), off);
+    }
+  }
+};
+
+// vmcnt wait with a run-time count that is a multiple of STEP below 4*STEP.
+template <int STEP>
+__device__ __forceinline__ void wait_vmcnt_steps(int steps) {
+  if (steps <= 0) wait_vmcnt<0>();
+  else if (steps == 1) wait_vmcnt<STEP < 64 ? STEP : 63>();
+  else if (steps == 2) wait_vmcnt<2 * STEP < 64 ? 2 * STEP : 63>();
+  else wait_vmcnt<3 * STEP < 64 ? 3 * STEP : 63>();
+}
+
+// Workgroup barrier that also orders this wave's LDS accesses before it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int BN>
+struct Staging {
+  static constexpr int PITCH = BN * 2 + 16;  // padding spreads rows over banks
+};
+
+// ======================================================= NT, single schedule
+
+template <typename T, int BM, int BN, int BK, int S>
+struct SwapCfg {
+  static constexpr int THREADS = 256;
+  static constexpr int WAVES = 4;
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  using Loader = SlotLoader<BM, BN, BK>;
+  static constexpr int PER_WAVE = Loader::INSTR / WAVES;  // loads per wave per tile
+  static constexpr int RING_BYTES = S * Loader::SLOT_BYTES;
+  static constexpr int STAGE_BYTES = BM * Staging<BN>::PITCH;
+  static constexpr int LDS_BYTES = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
+  static_assert(Loader::INSTR % WAVES == 0, "loads split evenly");
+  static_assert(S == 1 || (S - 1) * PER_WAVE < 64, "in-flight loads fit vmcnt");
+};
+
+template <typename T, int BM, int BN, int BK, int S>
+__global__ void __launch_bounds__(256, 1)
+    nt_swap_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
+                   uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m) {
+  using Cfg = SwapCfg<T, BM, BN, BK, S>;
+  using Loader = typename Cfg::Loader;
+  using Row = RingRow<BK>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int bm, bn;
+  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &bm, &bn);
+  const int m0 = bm * BM, n0 = bn * BN;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  Loader ld;
+  ld.init(lhs, rhs, M, N, K, m0, n0);
+  WaveTile<T, Cfg::WM, Cfg::WN, BK> w;
+  w.zero();
+  const int n_k = (K + BK - 1) / BK;
+  auto slot_ptr = [&](int s) { return smem + s * Loader::SLOT_BYTES; };
+  auto compute = [&](int s) {
+    char *base = slot_ptr(s);
+    w.mma_ktile(base + wm * Cfg::WM * Row::ROW_BYTES, base + (BM + wn * Cfg::WN) * Row::ROW_BYTES, lane);
+  };
+  const int first = wave * Cfg::PER_WAVE;
+
+  if constexpr (S == 1) {
+    for (int t = 0; t < n_k; ++t) {
+      ld.template load<Cfg::PER_WAVE>(slot_ptr(0), t, first, lane);
+      wait_vmcnt<0>();
+      lds_barrier();
+      compute(0);
+      lds_barrier();
+    }
+  } else {
+    // prologue: tiles 0 .. S-2 in flight
+    for (int j = 0; j < S - 1 && j < n_k; ++j) ld.template load<Cfg::PER_WAVE>(slot_ptr(j), j, first, lane);
+    for (int t = 0; t < n_k; ++t) {
+      // tile t has landed once at most min(S-2, n_k-1-t) younger tiles are pending
+      const int younger = (n_k - 1 - t) < (S - 2) ? (n_k - 1 - t) : (S - 2);
+      wait_vmcnt_steps<Cfg::PER_WAVE>(younger);
+      lds_barrier();  // tile t visible to all; everyone is done with tile t-1
+      if (t + S - 1 < n_k) ld.template load<Cfg::PER_WAVE>(slot_ptr((t + S - 1) % S), t + S - 1, first, lane);
+      compute(t % S);
+    }
+  }
+  __syncthreads();  // ring no longer read: reuse it as the staging tile
+  w.stage(smem, Staging<BN>::PITCH, wm * Cfg::WM, wn * Cfg::WN, lane);
+  __syncthreads();
+  store_staged<BM, BN, Cfg::THREADS>(smem, Staging<BN>::PITCH, out, M, N, m0, n0, tid);
+}
+
+// ========================================================= NT, WS (credits)
+
+template <typename T, int BM, int BN, int BK, int S, int C, int P>
+struct WsCfg {
+  static constexpr int THREADS = (C + P) * kWave;
+  static constexpr int CM = 2;                // consumer grid: CM x (C / CM)
+  static constexpr int CN = C / CM;
+  static constexpr int WM = BM / CM, WN = BN / CN;
+  using Loader = SlotLoader<BM, BN, BK>;
+  static constexpr int PER_PRODUCER = Loader::INSTR / P;
+  static constexpr int LAG = S - 1;           // tiles a producer keeps in flight unsignalled
+  static constexpr int RING_BYTES = S * Loader::SLOT_BYTES;
+  static constexpr int STAGE_BYTES = BM * Staging<BN>::PITCH;
+  static constexpr int CTR_OFFSET = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
+  static constexpr int LDS_BYTES = CTR_OFFSET + 2 * S * 4;
+  static_assert(Loader::INSTR % P == 0, "loads split evenly over producers");
+  static_assert((LAG + 1) * PER_PRODUCER < 64, "in-flight loads fit vmcnt");
+  static_assert(LAG <= 3, "vmcnt wait table covers three tiles");
+};
+
+template <typename T, int BM, int BN, int BK, int S, int C, int P>
+__global__ void __launch_bounds__((C + P) * 64, 1)
+    nt_ws_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
+                 uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m,
+                 uint32_t max_polls, int skip_seed, uint32_t *err) {
+  using Cfg = WsCfg<T, BM, BN, BK, S, C, P>;
+  using Loader = typename Cfg::Loader;
+  using Row = RingRow<BK>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  uint32_t *full = reinterpret_cast<uint32_t *>(smem + Cfg::CTR_OFFSET);
+  uint32_t *empty = full + S;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int bm, bn;
+  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &bm, &bn);
+  const int m0 = bm * BM, n0 = bn * BN;
+  const int n_k = (K + BK - 1) / BK;
+  auto slot_ptr = [&](int s) { return smem + s * Loader::SLOT_BYTES; };
+
+  if (tid < 2 * S) full[tid] = 0u;  // full[0..S) and empty[0..S)
+  __syncthreads();
+
+  WaveTile<T, Cfg::WM, Cfg::WN, BK> w;
+  const int wm = wave / Cfg::CN, wn = wave % Cfg::CN;
+  if (wave < C) {
+    // ---------------------------------------------------------- consumer
+    if (!skip_seed)
+      for (int s = 0; s < S; ++s) credit_trigger(&empty[s]);  // every slot starts free
+    w.zero();
+    for (int t = 0; t < n_k; ++t) {
+      const int s = t % S;
+      const uint32_t round = (uint32_t)(t / S);
+      credit_wait(&full[s], (uint32_t)P * (round + 1u), max_polls, err);
+      char *base = slot_ptr(s);
+      w.mma_ktile(base + wm * Cfg::WM * Row::ROW_BYTES, base + (BM + wn * Cfg::WN) * Row::ROW_BYTES, lane);
+      wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
+      credit_trigger(&empty[s]);
+    }
+  } else {
+    // ---------------------------------------------------------- producer
+    Loader ld;
+    ld.init(lhs, rhs, M, N, K, m0, n0);
+    const int first = (wave - C) * Cfg::PER_PRODUCER;
+    for (int t = 0; t < n_k; ++t) {
+      const int s = t % S;
+      const uint32_t round = (uint32_t)(t / S);
+      credit_wait(&empty[s], (uint32_t)C * (round + 1u), max_polls, err);
+      ld.template load<Cfg::PER_PRODUCER>(slot_ptr(s), t, first, lane);
+      if (t >= Cfg::LAG) {
+        wait_vmcnt_steps<Cfg::PER_PRODUCER>(Cfg::LAG);  // tile t-LAG has landed
+        credit_trigger(&full[(t - Cfg::LAG) % S]);
+      }
+    }
+    for (int t = n_k - Cfg::LAG < 0 ? 0 : n_k - Cfg::LAG; t < n_k; ++t) {  // drain
+      wait_vmcnt_steps<Cfg::PER_PRODUCER>(n_k - 1 - t);
+      credit_trigger(&full[t % S]);
+    }
+  }
+  __syncthreads();  // all tiles consumed: the ring becomes the staging tile
+  if (wave < C) w.stage(smem, Staging<BN>::PITCH, wm * Cfg::WM, wn * Cfg::WN, lane);
+  __syncthreads();
+  store_staged<BM, BN, Cfg::THREADS>(smem, Staging<BN>::PITCH, out, M, N, m0, n0, tid);
+}
+
+}  // namespace pgemm

@@ -1,0 +1,140 @@
+// Consumer-side math and the output epilogue.
+//
+// A wave owns a WM x WN block of the output, held as (WM/32) x (WN/32) fp32
+// accumulators of v_mfma_f32_32x32x16.  Operand roles: src0 is the rhs
+// fragment (32 rows n) and src1 the lhs fragment (32 rows m), so each
+// accumulator holds a transposed 32x32 output block:
+//   lane l, register r of acc[i][j] ->
+//     out[m0 + 32 i + l % 32][n0 + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4],
+// i.e. registers 4q..4q+3 are four consecutive columns of one row, which the
+// epilogue writes as one 8-byte piece.
+//
+// Both fragments are read the same way from a ring slot: lane l reads row
+// (base + l % 32) at chunk 2 kk + l / 32 (eight consecutive k), for the k16
+// step kk of the tile.  Every output element accumulates the k16 steps in
+// increasing k, so any tile shape, stage count or variant gives the same
+// bits.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace pgemm {
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<_Float16> {
+  __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // fp32 -> binary16, round to nearest even (v_cvt_f16_f32 in the default mode)
+  __device__ __forceinline__ static u32x2 pack4(float a, float b, float c, float d) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    h4 h = {(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+    return __builtin_bit_cast(u32x2, h);
+  }
+};
+
+template <>
+struct Mfma<__bf16> {
+  __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // fp32 -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32)
+  __device__ __forceinline__ static u32x2 pack4(float a, float b, float c, float d) {
+    typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+    b4 h = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+    return __builtin_bit_cast(u32x2, h);
+  }
+};
+
+template <typename T, int WM, int WN, int BK>
+struct WaveTile {
+  static constexpr int TM = WM / 32;
+  static constexpr int TN = WN / 32;
+  using Row = RingRow<BK>;
+  f32x16 acc[TM][TN];
+
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  }
+
+  // One K tile from a ring slot.  a_rows / b_rows: LDS address of the first
+  // of this wave's lhs / rhs rows in the slot; both are multiples of 32 rows
+  // from the tile start, so the swizzle term depends on l % 32 only.
+  __device__ __forceinline__ void mma_ktile(const char *a_rows, const char *b_rows, int lane) {
+    const int r = lane & 31;
+    const int hi = lane >> 5;
+    const int s = Row::swz(r);
+    const char *a_lane = a_rows + r * Row::ROW_BYTES;
+    const char *b_lane = b_rows + r * Row::ROW_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int p = ((2 * kk + hi) ^ s) * 16;
+      u32x4 af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const u32x4 *>(a_lane + 32 * i * Row::ROW_BYTES + p);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bf[j] = *reinterpret_cast<const u32x4 *>(b_lane + 32 * j * Row::ROW_BYTES + p);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T>::run(bf[j], af[i], acc[i][j]);
+    }
+  }
+
+  // Rounds the accumulators to T and writes them into an LDS staging tile
+  // (row pitch `pitch` bytes) at this wave's (row0, col0).
+  __device__ __forceinline__ void stage(char *st, int pitch, int row0, int col0, int lane) const {
+    const int r = lane & 31;
+    const int hi = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16 &a = acc[i][j];
+          u32x2 v = Mfma<T>::pack4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+          char *dst = st + (row0 + 32 * i + r) * pitch + (col0 + 32 * j + 8 * q + 4 * hi) * 2;
+          *reinterpret_cast<u32x2 *>(dst) = v;
+        }
+  }
+};
+
+// Copies a staged BM x BN tile (2-byte elements, row pitch `pitch` bytes) to
+// out[m0.., n0..] with 16-byte stores where the row piece is in range and
+// aligned, element stores at a ragged right edge, nothing past M.
+template <int BM, int BN, int THREADS>
+__device__ __forceinline__ void store_staged(const char *st, int pitch, uint16_t *out, int M, int N,
+                                             int m0, int n0, int tid) {
+  constexpr int CH = BN / 8;  // 16-byte pieces per tile row
+  const bool vec_ok = (N % 8) == 0;
+  for (int idx = tid; idx < BM * CH; idx += THREADS) {
+    const int row = idx / CH;
+    const int c = idx % CH;
+    const int gm = m0 + row;
+    const int gn = n0 + 8 * c;
+    if (gm >= M || gn >= N) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(st + row * pitch + c * 16);
+    uint16_t *dst = out + (int64_t)gm * N + gn;
+    if (vec_ok && gn + 8 <= N) {
+      *reinterpret_cast<u32x4 *>(dst) = v;
+    } else {
+      const uint16_t *e = reinterpret_cast<const uint16_t *>(&v);
+      for (int x = 0; x < 8 && gn + x < N; ++x) dst[x] = e[x];
+    }
+  }
+}
+
+}  // namespace pgemm

@@ -1,0 +1,99 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol its header
+declares, plans launches, and rejects bad arguments before any HIP call.
+Nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from software_pipelined_tiled_pipeline_amd import pgemm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pgemm.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_STAGES, ERR_ALIGN, ERR_LDS = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pgemm.LIB_PATH):
+        pytest.fail("libpgemm.so is not built (run __graft_entry__.build())")
+    return pgemm.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pgemm_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_messages(L):
+    assert pgemm.abi_version() == 1
+    for code in range(9):
+        assert pgemm.strerror(code) and pgemm.strerror(code) != "unknown status"
+    assert pgemm.strerror(99) == "unknown status"
+
+
+def test_query_geometry(L):
+    q = pgemm.pgemm_query("s32_nn", 0, 128, 256, 256)
+    assert (q["block_m"], q["block_n"], q["block_k"], q["stages"]) == (16, 16, 16, 2)
+    assert q["grid"] == 8 * 16 and q["threads"] == 256 and q["k_tiles"] == 16
+    q = pgemm.pgemm_query("nt_swap", 0, 8192, 8192, 8192)
+    assert q["stages"] == 2 and q["producer_waves"] == 0
+    assert q["grid"] == (8192 // q["block_m"]) * (8192 // q["block_n"])
+    for s in (1, 2, 3, 4):
+        q = pgemm.pgemm_query("nt_ws", s, 4095, 1000, 1000)
+        assert q["stages"] == s and q["producer_waves"] > 0 and q["consumer_waves"] > 0
+        assert q["lds_bytes"] <= 160 * 1024
+        assert q["threads"] == 64 * (q["producer_waves"] + q["consumer_waves"])
+        assert q["k_tiles"] == -(-1000 // q["block_k"])
+        # the ring holds `stages` versions of the (A, B) tile pair
+        ring = s * (q["block_m"] + q["block_n"]) * q["block_k"] * 2
+        assert ring <= q["lds_bytes"]
+    assert pgemm.pgemm_query("nt_ws", 0, 64, 64, 64)["stages"] == 4
+
+
+@pytest.mark.parametrize("op,stages", [("s32_nn", 3), ("nt_swap", 3), ("nt_ws", 5), ("nt_ws", -1)])
+def test_query_rejects_stages(L, op, stages):
+    info = pgemm.KernelInfo()
+    assert L.pgemm_query(pgemm.OPS[op], stages, 64, 64, 64, ctypes.byref(info)) == ERR_STAGES
+
+
+def test_query_rejects_shapes(L):
+    info = pgemm.KernelInfo()
+    assert L.pgemm_query(1, 0, -1, 64, 64, ctypes.byref(info)) == ERR_SHAPE
+    assert L.pgemm_query(1, 0, 64, 2 ** 31, 64, ctypes.byref(info)) == ERR_SHAPE
+    assert L.pgemm_query(2, 0, 64, 64, 2 ** 22, ctypes.byref(info)) == ERR_SHAPE
+    assert L.pgemm_query(0, 0, 64, 64, 2 ** 22, ctypes.byref(info)) == OK
+    assert L.pgemm_query(1, 0, 64, 64, 64, None) == ERR_NULL
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("name", pgemm.GEMM_SYMBOLS)
+def test_argument_errors_before_any_hip_call(L, name):
+    f = getattr(L, name)
+    nt = name != "pgemm_s32_nn"
+    assert f(None, FAKE, FAKE, 64, 64, 64, 0, None) == ERR_NULL
+    assert f(FAKE, None, FAKE, 64, 64, 64, 0, None) == ERR_NULL
+    assert f(FAKE, FAKE, None, 64, 64, 64, 0, None) == ERR_NULL
+    assert f(FAKE + 2, FAKE, FAKE, 64, 64, 64, 0, None) == ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE + 8, 64, 64, 64, 0, None) == ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, -1, 64, 64, 0, None) == ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 64, 64, 2 ** 31, 0, None) == ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 64, 64, 64, 7, None) == ERR_STAGES
+    if nt:
+        assert f(FAKE, FAKE, FAKE, 64, 64, 12, 0, None) == ERR_ALIGN  # K not a multiple of 8
+    # empty outputs: nothing to launch; pointers to empty matrices may be NULL
+    assert f(None, FAKE, None, 0, 64, 64, 0, None) == OK
+    assert f(FAKE, None, None, 64, 0, 64, 0, None) == OK
+    assert f(None, None, None, 0, 0, 64, 0, None) == OK

@@ -1,0 +1,240 @@
+"""GPU parity: every pgemm entry point against the CPU oracle.
+
+int32 results must be bit-exact.  f16/bf16 results must satisfy, element by
+element, |gpu - ref| <= 1e-3 * sum_k |a*b| + ulp(RNE(ref)) in the output
+type, with ref and sum_k |a*b| from the binary64 oracle.  Small shapes are
+compared in full; the full-size workloads are compared on sampled elements
+(the oracle computes each one alone) plus whole edge rows and columns, and
+across stages and variants for bit identity (every kernel accumulates the
+k16 MFMA steps in the same order).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from software_pipelined_tiled_pipeline_amd import inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from software_pipelined_tiled_pipeline_amd import pgemm
+    pgemm.lib()
+    return pgemm
+
+
+def dev_half(bits, fmt):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    return t.view(torch.float16 if fmt == "f16" else torch.bfloat16)
+
+
+def host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_nt(pg, fmt, variant, A, B, stages, dA=None, dB=None):
+    dA = dev_half(A, fmt) if dA is None else dA
+    dB = dev_half(B, fmt) if dB is None else dB
+    name = f"pgemm_{fmt}_nt" + ("_ws" if variant == "ws" else "")
+    out = getattr(pg, name)(dA, dB, stages=stages)
+    torch.cuda.synchronize()
+    return host_bits(out)
+
+
+def assert_within_bound(fmt, got, ref, mag, what):
+    bad, worst = oracle.check_nt(fmt, got, ref, mag)
+    assert bad == 0, f"{what}: {bad} elements outside the bound (worst err/bound {worst:.3g})"
+    return worst
+
+
+VARIANTS = [("swap", 1), ("swap", 2), ("ws", 1), ("ws", 2), ("ws", 3), ("ws", 4)]
+
+
+# ------------------------------------------------------------------ int32
+
+@pytest.mark.parametrize("stages", [1, 2])
+def test_s32_workload_128x256x256(pg, stages):
+    M, N, K = 128, 256, 256
+    A, B = inputs.make_operands("s32_nn", M, N, K, inputs.workload_seed(1))
+    out = pg.pgemm_s32_nn(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), stages=stages)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.gemm_s32_nn(A, B))
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 53, 29), (1, 1, 1), (16, 16, 16), (17, 15, 33), (200, 3, 0), (5, 300, 1)])
+@pytest.mark.parametrize("stages", [1, 2])
+def test_s32_ragged_and_wrapping(pg, M, N, K, stages):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    A = rng.integers(-2 ** 31, 2 ** 31, (M, K)).astype(np.int32)
+    B = rng.integers(-2 ** 31, 2 ** 31, (K, N)).astype(np.int32)
+    out = pg.pgemm_s32_nn(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), stages=stages)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.gemm_s32_nn(A, B))
+
+
+# ------------------------------------------------- NT, full comparisons
+
+SMALL = [(520, 300, 200), (257, 129, 136), (64, 64, 8), (1, 1, 8), (300, 1000, 64), (513, 257, 1000)]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_nt_small_all_variants(pg, fmt, M, N, K):
+    kind = "f16_nt" if fmt == "f16" else "bf16_nt"
+    A, B = inputs.make_operands(kind, M, N, K, 1000 + M + N + K)
+    ref, mag = oracle.gemm_nt(fmt, A, B)
+    dA, dB = dev_half(A, fmt), dev_half(B, fmt)
+    first = None
+    for variant, s in VARIANTS:
+        got = run_nt(pg, fmt, variant, A, B, s, dA, dB)
+        assert_within_bound(fmt, got, ref, mag, f"{fmt} {variant} S={s} {M}x{N}x{K}")
+        if first is None:
+            first = got
+        else:
+            assert np.array_equal(got, first), f"{variant} S={s} differs in bits from swap S=1"
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_nt_k_zero_gives_zeros(pg, fmt):
+    A = np.zeros((70, 0), np.uint16)
+    B = np.zeros((90, 0), np.uint16)
+    for variant, s in VARIANTS:
+        dA = torch.zeros((70, 0), dtype=torch.float16 if fmt == "f16" else torch.bfloat16, device="cuda")
+        dB = torch.zeros((90, 0), dtype=dA.dtype, device="cuda")
+        name = f"pgemm_{fmt}_nt" + ("_ws" if variant == "ws" else "")
+        out = getattr(pg, name)(dA, dB, out=torch.full((70, 90), 7.0, dtype=dA.dtype, device="cuda"), stages=s)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out).item() == 0
+
+
+@pytest.mark.parametrize("variant,stages", VARIANTS)
+def test_nt_closed_forms(pg, variant, stages):
+    # identity: lhs * I^T = lhs exactly
+    K = 384
+    A = inputs.f16_uniform1((300, K), 3, 0)
+    I = np.where(np.eye(K, dtype=bool), np.uint16(0x3C00), np.uint16(0))
+    assert np.array_equal(run_nt(pg, "f16", variant, A, I, stages), A)
+    # all ones: exactly K (4096 is a binary16 value)
+    ones_a = np.full((260, 4096), 0x3C00, np.uint16)
+    ones_b = np.full((130, 4096), 0x3C00, np.uint16)
+    got = run_nt(pg, "f16", variant, ones_a, ones_b, stages)
+    assert np.all(got == np.float16(4096).view(np.uint16))
+    # rank one: only k = 0 is non-zero, so out = RNE(u_m * v_n) with one rounding
+    for fmt, kind in (("f16", "f16_nt"), ("bf16", "bf16_nt")):
+        u, v = inputs.make_operands(kind, 270, 140, 8, 77)
+        u[:, 1:] = 0
+        v[:, 1:] = 0
+        ref, _ = oracle.gemm_nt(fmt, u, v)
+        assert np.array_equal(run_nt(pg, fmt, variant, u, v, stages), oracle.encode(fmt, ref))
+
+
+# ------------------------------------------------------ full-size workloads
+
+def sample_entries(M, N, count, seed):
+    rng = np.random.default_rng(seed)
+    mi = [rng.integers(0, M, count)]
+    ni = [rng.integers(0, N, count)]
+    for m in sorted({0, M - 1}):          # whole first and last rows
+        mi.append(np.full(N, m))
+        ni.append(np.arange(N))
+    for n in sorted({0, N - 1}):          # whole first and last columns
+        mi.append(np.arange(M))
+        ni.append(np.full(M, n))
+    return np.concatenate(mi), np.concatenate(ni)
+
+
+def check_sampled(fmt, A, B, outs, seed, count=2048):
+    M, N = A.shape[0], B.shape[0]
+    mi, ni = sample_entries(M, N, count, seed)
+    ref, mag = oracle.gemm_nt_entries(fmt, A, B, mi, ni)
+    worst = 0.0
+    for what, got in outs.items():
+        worst = max(worst, assert_within_bound(fmt, got[mi, ni], ref, mag, what))
+    return worst
+
+
+@pytest.fixture(scope="module")
+def w2():
+    return inputs.make_operands("f16_nt", 4096, 4096, 4096, inputs.workload_seed(2))
+
+
+def test_workload_f16_4096_swap2_vs_ws4(pg, w2):
+    A, B = w2
+    dA, dB = dev_half(A, "f16"), dev_half(B, "f16")
+    outs = {
+        "swap S=2": run_nt(pg, "f16", "swap", A, B, 2, dA, dB),
+        "ws S=4": run_nt(pg, "f16", "ws", A, B, 4, dA, dB),
+    }
+    check_sampled("f16", A, B, outs, 2)
+    assert np.array_equal(outs["swap S=2"], outs["ws S=4"])
+
+
+def test_determinism_repeats(pg, w2):
+    A, B = w2
+    dA, dB = dev_half(A, "f16"), dev_half(B, "f16")
+    first = run_nt(pg, "f16", "ws", A, B, 4, dA, dB)
+    for _ in range(5):
+        assert np.array_equal(run_nt(pg, "f16", "ws", A, B, 4, dA, dB), first)
+
+
+def test_workload_f16_8192_stage_sweep(pg):
+    A, B = inputs.make_operands("f16_nt", 8192, 8192, 8192, inputs.workload_seed(3))
+    dA, dB = dev_half(A, "f16"), dev_half(B, "f16")
+    outs = {f"ws S={s}": run_nt(pg, "f16", "ws", A, B, s, dA, dB) for s in (1, 2, 3, 4)}
+    outs["swap S=2"] = run_nt(pg, "f16", "swap", A, B, 2, dA, dB)
+    check_sampled("f16", A, B, outs, 3, count=1024)
+    first = outs["ws S=1"]
+    for k, v in outs.items():
+        assert np.array_equal(v, first), f"{k} differs in bits from ws S=1"
+
+
+@pytest.mark.parametrize("variant,stages", [("ws", 4), ("ws", 2), ("swap", 2), ("swap", 1)])
+def test_workload_bf16_ragged_4095x1000x1000(pg, variant, stages):
+    M, N, K = 4095, 1000, 1000
+    A, B = inputs.make_operands("bf16_nt", M, N, K, inputs.workload_seed(4))
+    ref, mag = oracle.gemm_nt("bf16", A, B)
+    got = run_nt(pg, "bf16", variant, A, B, stages)
+    q = pg.pgemm_query("nt_ws" if variant == "ws" else "nt_swap", stages, M, N, K)
+    # report the edges separately: last partial row tile, last partial column tile
+    em = (M // q["block_m"]) * q["block_m"]
+    en = (N // q["block_n"]) * q["block_n"]
+    assert_within_bound("bf16", got[em:], ref[em:], mag[em:], "partial M tile")
+    assert_within_bound("bf16", got[:, en:], ref[:, en:], mag[:, en:], "partial N tile")
+    assert_within_bound("bf16", got, ref, mag, f"bf16 {variant} S={stages}")
+
+
+def test_workload_f16_skinny_128x8192x16384(pg):
+    A, B = inputs.make_operands("f16_nt", 128, 8192, 16384, inputs.workload_seed(5))
+    dA, dB = dev_half(A, "f16"), dev_half(B, "f16")
+    outs = {f"ws S={s}": run_nt(pg, "f16", "ws", A, B, s, dA, dB) for s in (2, 3, 4)}
+    outs["swap S=2"] = run_nt(pg, "f16", "swap", A, B, 2, dA, dB)
+    check_sampled("f16", A, B, outs, 5, count=2048)
+    first = outs["ws S=2"]
+    for k, v in outs.items():
+        assert np.array_equal(v, first), k
+
+
+# ----------------------------------------------------- credit protocol
+
+def test_missing_seed_times_out_instead_of_hanging(pg):
+    # Without the consumers' initial empty credits the producers' first wait
+    # can never succeed.  With a small poll limit every wait gives up, the
+    # kernel still exits, and the host sees PGEMM_ERR_TIMEOUT.
+    A, B = inputs.make_operands("f16_nt", 256, 128, 128, 9)
+    dA, dB = dev_half(A, "f16"), dev_half(B, "f16")
+    assert pg.pgemm_sync_status() == 0
+    try:
+        pg.pgemm_set_ws_debug(max_polls=2000, skip_seed=True)
+        pg.pgemm_f16_nt_ws(dA, dB, stages=2)
+        assert pg.pgemm_sync_status() == 7  # PGEMM_ERR_TIMEOUT
+    finally:
+        pg.pgemm_set_ws_debug(0, False)
+    assert pg.pgemm_sync_status() == 0
+    got = run_nt(pg, "f16", "ws", A, B, 2, dA, dB)
+    ref, mag = oracle.gemm_nt("f16", A, B)
+    assert_within_bound("f16", got, ref, mag, "after reset")
+    assert pg.pgemm_sync_status() == 0
