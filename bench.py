@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the software-pipelined f16 NT GEMM on one MI355X.
+
+Workload: out f16[8192, 8192] = lhs f16[8192, 8192] . rhs f16[8192, 8192]^T
+with fp32 accumulation, operands uniform in [-1, 1) from the seeded SplitMix64
+generator.  A step is one GEMM call of the producer/consumer kernel
+(pgemm_f16_nt_ws) at the stage count that the untimed sweep over {1, 2, 3, 4}
+finds fastest; the single-schedule kernel is swept too and reported beside it.
+
+Prints one JSON line (rank 0) with TFLOP/s, the roofline position of the
+kernel (average launch time from HIP events on the launch stream), and the
+CPU oracle timed on a bounded sample of the same product.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2516.6   # 256 CUs x 4096 flop/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (M, N, K, seed workload index)
+    "f16_nt_8192": (8192, 8192, 8192, 3),
+    "f16_nt_4096": (4096, 4096, 4096, 2),
+    "f16_nt_skinny": (128, 8192, 16384, 5),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "software_pipelined_tiled_pipeline_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, workload: str, stages: int):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    want = kernel_source_hash()
+    for line in open(path):
+        m = re.match(r"\s*traffic\s+(\S+)\s+(\S+)\s+S=(\d+)\s+src=(\S+)\s+bytes=(\d+)", line)
+        if m and m.group(1) == kernel and m.group(2) == workload and int(m.group(3)) == stages \
+                and m.group(4) == want:
+            return int(m.group(5))
+    return None
+
+
+def time_launches(fn, reps, stream):
+    """Per-launch durations (ms) from HIP events on the launch stream."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def cpu_baseline(A, B, M, N, K, budget_s: float):
+    """The oracle, as it stands, on a leading block of output rows."""
+    import oracle
+    rows = 2
+    t = 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm_nt("f16", A[:rows], B)
+        t = time.perf_counter() - t0
+        if t * 4 > budget_s or rows * 4 > M:
+            break
+        rows *= 4
+    flops = 2.0 * rows * N * K
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"first {rows} of {M} output rows ({rows}x{N}x{K}), {t:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="f16_nt_8192")
+    ap.add_argument("--variant", choices=["ws", "swap"], default="ws")
+    ap.add_argument("--stages", type=int, default=0, help="0: fastest of the sweep")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(a multi-GPU run would split the output columns across GPUs; it is not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from software_pipelined_tiled_pipeline_amd import inputs, pgemm
+
+    pgemm.lib()  # fails loudly if the HIP library is missing
+    M, N, K, widx = WORKLOADS[args.workload]
+    log(f"[bench] generating {args.workload} operands {M}x{N}x{K}")
+    A, B = inputs.make_operands("f16_nt", M, N, K, inputs.workload_seed(widx))
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(A.view(np.int16)).to(dev).view(torch.float16)
+    dB = torch.from_numpy(B.view(np.int16)).to(dev).view(torch.float16)
+    out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+    flops = 2.0 * M * N * K
+
+    fns = {"ws": pgemm.pgemm_f16_nt_ws, "swap": pgemm.pgemm_f16_nt}
+    sweep = {}
+    for variant, stage_set in (("ws", (1, 2, 3, 4)), ("swap", (1, 2))):
+        for s in stage_set:
+            f = fns[variant]
+            call = lambda f=f, s=s: f(dA, dB, out=out, stages=s)
+            time_launches(call, 2, stream)
+            ms = float(np.median(time_launches(call, 5, stream)))
+            sweep[f"{variant} S={s}"] = round(flops / (ms * 1e-3) / 1e12, 1)
+            log(f"[bench] sweep {variant} S={s}: {ms * 1e3:.1f} us, {sweep[f'{variant} S={s}']} TFLOP/s")
+    stages = args.stages
+    if stages == 0:
+        cands = {k: v for k, v in sweep.items() if k.startswith(args.variant + " ")}
+        stages = int(max(cands, key=cands.get).split("S=")[1])
+    fn = fns[args.variant]
+    step = lambda: fn(dA, dB, out=out, stages=stages)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps of {args.variant} S={stages}")
+    t0 = time.perf_counter()
+    durs = time_launches(step, args.steps, stream)
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    if pgemm.pgemm_sync_status() != 0:
+        raise RuntimeError("a credit wait gave up during the timed region")
+    value = flops * args.steps / wall / 1e12
+    kern_ms = float(np.mean(durs))
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+
+    # spot check of the timed output against the oracle
+    import oracle
+    rng = np.random.default_rng(123)
+    mi, ni = rng.integers(0, M, 256), rng.integers(0, N, 256)
+    ref, mag = oracle.gemm_nt_entries("f16", A, B, mi, ni)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)[mi, ni]
+    bad, worst = oracle.check_nt("f16", got, ref, mag)
+    if bad:
+        raise RuntimeError(f"timed output fails the oracle on {bad} of 256 sampled elements")
+
+    kname = "nt_ws_kernel" if args.variant == "ws" else "nt_swap_kernel"
+    traffic = recorded_traffic(kname, args.workload, stages)
+    result = {
+        "metric": "TFLOP/s (and % of MFMA peak) for f16 NT GEMM 8192^3, 1 MI355X"
+        if args.workload == "f16_nt_8192" else f"TFLOP/s for f16 NT GEMM {M}x{N}x{K}, 1 MI355X",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"f16 NT GEMM M={M} N={N} K={K}, operands uniform[-1,1), fp32 accumulation, "
+                        f"{'producer/consumer credits' if args.variant == 'ws' else 'single-schedule swap'}",
+            "M": M, "N": N, "K": K,
+            "variant": args.variant,
+            "stages": stages,
+            "pct_of_mfma_peak": round(100.0 * value / PEAK_F16_TFLOPS, 1),
+            "stage_sweep_tflops": sweep,
+            "parity": {"sampled": 256, "violations": bad, "worst_err_over_bound": round(worst, 4)},
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": kname,
+            "kernel_avg_us": round(kern_ms * 1e3, 2),
+        },
+    }
+    if args.workload == "f16_nt_skinny":
+        alg_bytes = (M * K + N * K + M * N) * 2
+        result["roofline"].update({
+            "bound": "hbm", "achieved": round(alg_bytes / (kern_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(alg_bytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample of the same product")
+        result["cpu_baseline"] = cpu_baseline(A, B, M, N, K, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

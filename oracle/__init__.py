@@ -64,8 +64,15 @@ def _load():
         lib.pgo_check_nt.argtypes = [ctypes.c_int, P, P, P, I64, ctypes.c_double,
                                      ctypes.POINTER(ctypes.c_double)]
         lib.pgo_check_nt.restype = ctypes.c_int64
+        lib.pgo_threads.argtypes = []
+        lib.pgo_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().pgo_threads())
 
 
 def _fmt(fmt) -> int:

@@ -30,6 +30,9 @@
  * are independent of any other half-precision code in the repository.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -146,6 +149,15 @@ void pgo_encode(int fmt, const double *in, uint16_t *out, int64_t n) {
 void pgo_ulp(int fmt, const double *in, double *out, int64_t n) {
   for (int64_t i = 0; i < n; ++i)
     out[i] = fmt == PGO_F16 ? pgo_ulp_f16(in[i]) : pgo_ulp_bf16(in[i]);
+}
+
+/* Number of threads the OpenMP loops below use. */
+int pgo_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
 
 /* ----------------------------------------------------------------- GEMMs */
