@@ -149,53 +149,65 @@ struct Staging {
   static constexpr int PITCH = BN * 2 + 16;  // padding spreads rows over banks
 };
 
-// ======================================================= NT, single schedule
-
-template <typename T, int BM, int BN, int BK, int S>
-struct SwapCfg {
-  static constexpr int THREADS = 256;
-  static constexpr int WAVES = 4;
-  static constexpr int WM = BM / 2, WN = BN / 2;
+// Geometry of one NT kernel instance: output tile BM x BN, K tile BK, S ring
+// slots, WGM x WGN math waves (each owning a (BM/WGM) x (BN/WGN) block) and
+// P producer waves (0 for the single-schedule kernel).
+template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_, int P_>
+struct NtGeom {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
+  static constexpr int WGM = WGM_, WGN = WGN_, P = P_;
+  static constexpr int CW = WGM * WGN;  // math waves
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int THREADS = (CW + P) * kWave;
   using Loader = SlotLoader<BM, BN, BK>;
-  static constexpr int PER_WAVE = Loader::INSTR / WAVES;  // loads per wave per tile
+  static constexpr int LOADERS = P > 0 ? P : CW;  // waves that fill the ring
+  static constexpr int PER_LOADER = Loader::INSTR / LOADERS;
   static constexpr int RING_BYTES = S * Loader::SLOT_BYTES;
   static constexpr int STAGE_BYTES = BM * Staging<BN>::PITCH;
-  static constexpr int LDS_BYTES = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
-  static_assert(Loader::INSTR % WAVES == 0, "loads split evenly");
-  static_assert(S == 1 || (S - 1) * PER_WAVE < 64, "in-flight loads fit vmcnt");
+  static constexpr int CTR_OFFSET = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
+  static constexpr int LDS_BYTES = CTR_OFFSET + (P > 0 ? 2 * S * 4 : 0);
+  // a producer keeps up to S-1 tiles in flight before signalling the oldest
+  static constexpr int LAG = S - 1;
+  static_assert(Loader::INSTR % LOADERS == 0, "loads split evenly");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave blocks are whole 32x32 MFMA tiles");
+  static_assert(S <= 4, "vmcnt wait table covers three tiles in flight");
+  static_assert(S * PER_LOADER < 64, "in-flight loads fit the 6-bit vmcnt");
 };
 
-template <typename T, int BM, int BN, int BK, int S>
-__global__ void __launch_bounds__(256, 1)
+// ======================================================= NT, single schedule
+
+template <typename T, class G>
+__global__ void __launch_bounds__(G::THREADS)
     nt_swap_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
                    uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m) {
-  using Cfg = SwapCfg<T, BM, BN, BK, S>;
-  using Loader = typename Cfg::Loader;
-  using Row = RingRow<BK>;
+  static_assert(G::P == 0, "single-schedule kernel has no producer waves");
+  using Loader = typename G::Loader;
+  using Row = RingRow<G::BK>;
+  constexpr int S = G::S;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bm, bn;
   tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &bm, &bn);
-  const int m0 = bm * BM, n0 = bn * BN;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = bm * G::BM, n0 = bn * G::BN;
+  const int wm = wave / G::WGN, wn = wave % G::WGN;
 
   Loader ld;
   ld.init(lhs, rhs, M, N, K, m0, n0);
-  WaveTile<T, Cfg::WM, Cfg::WN, BK> w;
+  WaveTile<T, G::WM, G::WN, G::BK> w;
   w.zero();
-  const int n_k = (K + BK - 1) / BK;
+  const int n_k = (K + G::BK - 1) / G::BK;
   auto slot_ptr = [&](int s) { return smem + s * Loader::SLOT_BYTES; };
   auto compute = [&](int s) {
     char *base = slot_ptr(s);
-    w.mma_ktile(base + wm * Cfg::WM * Row::ROW_BYTES, base + (BM + wn * Cfg::WN) * Row::ROW_BYTES, lane);
+    w.mma_ktile(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
   };
-  const int first = wave * Cfg::PER_WAVE;
+  const int first = wave * G::PER_LOADER;
 
   if constexpr (S == 1) {
     for (int t = 0; t < n_k; ++t) {
-      ld.template load<Cfg::PER_WAVE>(slot_ptr(0), t, first, lane);
+      ld.template load<G::PER_LOADER>(slot_ptr(0), t, first, lane);
       wait_vmcnt<0>();
       lds_barrier();
       compute(0);
@@ -203,67 +215,50 @@ __global__ void __launch_bounds__(256, 1)
     }
   } else {
     // prologue: tiles 0 .. S-2 in flight
-    for (int j = 0; j < S - 1 && j < n_k; ++j) ld.template load<Cfg::PER_WAVE>(slot_ptr(j), j, first, lane);
+    for (int j = 0; j < S - 1 && j < n_k; ++j) ld.template load<G::PER_LOADER>(slot_ptr(j), j, first, lane);
     for (int t = 0; t < n_k; ++t) {
       // tile t has landed once at most min(S-2, n_k-1-t) younger tiles are pending
       const int younger = (n_k - 1 - t) < (S - 2) ? (n_k - 1 - t) : (S - 2);
-      wait_vmcnt_steps<Cfg::PER_WAVE>(younger);
+      wait_vmcnt_steps<G::PER_LOADER>(younger);
       lds_barrier();  // tile t visible to all; everyone is done with tile t-1
-      if (t + S - 1 < n_k) ld.template load<Cfg::PER_WAVE>(slot_ptr((t + S - 1) % S), t + S - 1, first, lane);
+      if (t + S - 1 < n_k) ld.template load<G::PER_LOADER>(slot_ptr((t + S - 1) % S), t + S - 1, first, lane);
       compute(t % S);
     }
   }
   __syncthreads();  // ring no longer read: reuse it as the staging tile
-  w.stage(smem, Staging<BN>::PITCH, wm * Cfg::WM, wn * Cfg::WN, lane);
+  w.stage(smem, Staging<G::BN>::PITCH, wm * G::WM, wn * G::WN, lane);
   __syncthreads();
-  store_staged<BM, BN, Cfg::THREADS>(smem, Staging<BN>::PITCH, out, M, N, m0, n0, tid);
+  store_staged<G::BM, G::BN, G::THREADS>(smem, Staging<G::BN>::PITCH, out, M, N, m0, n0, tid);
 }
 
 // ========================================================= NT, WS (credits)
 
-template <typename T, int BM, int BN, int BK, int S, int C, int P>
-struct WsCfg {
-  static constexpr int THREADS = (C + P) * kWave;
-  static constexpr int CM = 2;                // consumer grid: CM x (C / CM)
-  static constexpr int CN = C / CM;
-  static constexpr int WM = BM / CM, WN = BN / CN;
-  using Loader = SlotLoader<BM, BN, BK>;
-  static constexpr int PER_PRODUCER = Loader::INSTR / P;
-  static constexpr int LAG = S - 1;           // tiles a producer keeps in flight unsignalled
-  static constexpr int RING_BYTES = S * Loader::SLOT_BYTES;
-  static constexpr int STAGE_BYTES = BM * Staging<BN>::PITCH;
-  static constexpr int CTR_OFFSET = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
-  static constexpr int LDS_BYTES = CTR_OFFSET + 2 * S * 4;
-  static_assert(Loader::INSTR % P == 0, "loads split evenly over producers");
-  static_assert((LAG + 1) * PER_PRODUCER < 64, "in-flight loads fit vmcnt");
-  static_assert(LAG <= 3, "vmcnt wait table covers three tiles");
-};
-
-template <typename T, int BM, int BN, int BK, int S, int C, int P>
-__global__ void __launch_bounds__((C + P) * 64, 1)
+template <typename T, class G>
+__global__ void __launch_bounds__(G::THREADS)
     nt_ws_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
                  uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m,
                  uint32_t max_polls, int skip_seed, uint32_t *err) {
-  using Cfg = WsCfg<T, BM, BN, BK, S, C, P>;
-  using Loader = typename Cfg::Loader;
-  using Row = RingRow<BK>;
+  static_assert(G::P > 0, "producer/consumer kernel needs producer waves");
+  using Loader = typename G::Loader;
+  using Row = RingRow<G::BK>;
+  constexpr int S = G::S, C = G::CW, P = G::P;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  uint32_t *full = reinterpret_cast<uint32_t *>(smem + Cfg::CTR_OFFSET);
+  uint32_t *full = reinterpret_cast<uint32_t *>(smem + G::CTR_OFFSET);
   uint32_t *empty = full + S;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bm, bn;
   tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &bm, &bn);
-  const int m0 = bm * BM, n0 = bn * BN;
-  const int n_k = (K + BK - 1) / BK;
+  const int m0 = bm * G::BM, n0 = bn * G::BN;
+  const int n_k = (K + G::BK - 1) / G::BK;
   auto slot_ptr = [&](int s) { return smem + s * Loader::SLOT_BYTES; };
 
   if (tid < 2 * S) full[tid] = 0u;  // full[0..S) and empty[0..S)
   __syncthreads();
 
-  WaveTile<T, Cfg::WM, Cfg::WN, BK> w;
-  const int wm = wave / Cfg::CN, wn = wave % Cfg::CN;
+  WaveTile<T, G::WM, G::WN, G::BK> w;
+  const int wm = wave / G::WGN, wn = wave % G::WGN;
   if (wave < C) {
     // ---------------------------------------------------------- consumer
     if (!skip_seed)
@@ -274,7 +269,7 @@ __global__ void __launch_bounds__((C + P) * 64, 1)
       const uint32_t round = (uint32_t)(t / S);
       credit_wait(&full[s], (uint32_t)P * (round + 1u), max_polls, err);
       char *base = slot_ptr(s);
-      w.mma_ktile(base + wm * Cfg::WM * Row::ROW_BYTES, base + (BM + wn * Cfg::WN) * Row::ROW_BYTES, lane);
+      w.mma_ktile(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
       wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
       credit_trigger(&empty[s]);
     }
@@ -282,26 +277,26 @@ __global__ void __launch_bounds__((C + P) * 64, 1)
     // ---------------------------------------------------------- producer
     Loader ld;
     ld.init(lhs, rhs, M, N, K, m0, n0);
-    const int first = (wave - C) * Cfg::PER_PRODUCER;
+    const int first = (wave - C) * G::PER_LOADER;
     for (int t = 0; t < n_k; ++t) {
       const int s = t % S;
       const uint32_t round = (uint32_t)(t / S);
       credit_wait(&empty[s], (uint32_t)C * (round + 1u), max_polls, err);
-      ld.template load<Cfg::PER_PRODUCER>(slot_ptr(s), t, first, lane);
-      if (t >= Cfg::LAG) {
-        wait_vmcnt_steps<Cfg::PER_PRODUCER>(Cfg::LAG);  // tile t-LAG has landed
-        credit_trigger(&full[(t - Cfg::LAG) % S]);
+      ld.template load<G::PER_LOADER>(slot_ptr(s), t, first, lane);
+      if (t >= G::LAG) {
+        wait_vmcnt_steps<G::PER_LOADER>(G::LAG);  // tile t-LAG has landed
+        credit_trigger(&full[(t - G::LAG) % S]);
       }
     }
-    for (int t = n_k - Cfg::LAG < 0 ? 0 : n_k - Cfg::LAG; t < n_k; ++t) {  // drain
-      wait_vmcnt_steps<Cfg::PER_PRODUCER>(n_k - 1 - t);
+    for (int t = n_k - G::LAG < 0 ? 0 : n_k - G::LAG; t < n_k; ++t) {  // drain
+      wait_vmcnt_steps<G::PER_LOADER>(n_k - 1 - t);
       credit_trigger(&full[t % S]);
     }
   }
   __syncthreads();  // all tiles consumed: the ring becomes the staging tile
-  if (wave < C) w.stage(smem, Staging<BN>::PITCH, wm * Cfg::WM, wn * Cfg::WN, lane);
+  if (wave < C) w.stage(smem, Staging<G::BN>::PITCH, wm * G::WM, wn * G::WN, lane);
   __syncthreads();
-  store_staged<BM, BN, Cfg::THREADS>(smem, Staging<BN>::PITCH, out, M, N, m0, n0, tid);
+  store_staged<G::BM, G::BN, G::THREADS>(smem, Staging<G::BN>::PITCH, out, M, N, m0, n0, tid);
 }
 
 }  // namespace pgemm

@@ -11,7 +11,7 @@
 #include <mutex>
 
 #include "../../include/pgemm.h"
-#include "kernels.hpp"
+#include "instances.hpp"
 
 // Device-side error word: a credit wait that runs past its poll limit sets
 // bit 0.  One copy per device; the host reaches it through its address.
@@ -35,41 +35,19 @@ std::atomic<int> g_skip_seed{0};
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <class Cfg, int BM, int BN, int BK, int S>
-void fill_swap(pgemm_kernel_info *i, int64_t M, int64_t N, int64_t K) {
-  i->block_m = BM;
-  i->block_n = BN;
-  i->block_k = BK;
-  i->stages = S;
-  i->producer_waves = 0;
-  i->consumer_waves = Cfg::WAVES;
-  i->threads = Cfg::THREADS;
-  i->lds_bytes = Cfg::LDS_BYTES;
-  i->grid = cdiv(M, BM) * cdiv(N, BN);
-  i->k_tiles = cdiv(K, BK);
+template <class G>
+void fill_nt(pgemm_kernel_info *i, int64_t M, int64_t N, int64_t K) {
+  i->block_m = G::BM;
+  i->block_n = G::BN;
+  i->block_k = G::BK;
+  i->stages = G::S;
+  i->producer_waves = G::P;
+  i->consumer_waves = G::CW;
+  i->threads = G::THREADS;
+  i->lds_bytes = G::LDS_BYTES;
+  i->grid = cdiv(M, G::BM) * cdiv(N, G::BN);
+  i->k_tiles = cdiv(K, G::BK);
 }
-
-template <class Cfg, int BM, int BN, int BK, int S, int C, int P>
-void fill_ws(pgemm_kernel_info *i, int64_t M, int64_t N, int64_t K) {
-  i->block_m = BM;
-  i->block_n = BN;
-  i->block_k = BK;
-  i->stages = S;
-  i->producer_waves = P;
-  i->consumer_waves = C;
-  i->threads = Cfg::THREADS;
-  i->lds_bytes = Cfg::LDS_BYTES;
-  i->grid = cdiv(M, BM) * cdiv(N, BN);
-  i->k_tiles = cdiv(K, BK);
-}
-
-// Instances.  Single schedule: 256 x 256 output tile, four waves of
-// 128 x 128, K tile 64.  Producer/consumer: 256 x 128 output tile, four
-// consumer waves of 128 x 64 and four producer waves; K tile 64 for up to
-// three slots, 32 for four (four 48 KiB slots would not fit in LDS).
-#define SWAP_CFG(T, S) SwapCfg<T, 256, 256, 64, S>
-#define WS_BK(S) ((S) == 4 ? 32 : 64)
-#define WS_CFG(T, S) WsCfg<T, 256, 128, WS_BK(S), S, 4, 4>
 
 pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, pgemm_kernel_info *info,
                   int *stages_out) {
@@ -93,20 +71,20 @@ pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, pgem
     }
     case PGEMM_OP_NT_SWAP: {
       if (K >= kMaxKNt) return PGEMM_ERR_SHAPE;
-      int s = stages == 0 ? 2 : stages;
-      if (s == 1) fill_swap<SWAP_CFG(_Float16, 1), 256, 256, 64, 1>(info, M, N, K);
-      else if (s == 2) fill_swap<SWAP_CFG(_Float16, 2), 256, 256, 64, 2>(info, M, N, K);
+      int s = stages == 0 ? kSwapDefaultStages : stages;
+      if (s == 1) fill_nt<SwapGeom<1>>(info, M, N, K);
+      else if (s == 2) fill_nt<SwapGeom<2>>(info, M, N, K);
       else return PGEMM_ERR_STAGES;
       *stages_out = s;
       break;
     }
     case PGEMM_OP_NT_WS: {
       if (K >= kMaxKNt) return PGEMM_ERR_SHAPE;
-      int s = stages == 0 ? 4 : stages;
-      if (s == 1) fill_ws<WS_CFG(_Float16, 1), 256, 128, WS_BK(1), 1, 4, 4>(info, M, N, K);
-      else if (s == 2) fill_ws<WS_CFG(_Float16, 2), 256, 128, WS_BK(2), 2, 4, 4>(info, M, N, K);
-      else if (s == 3) fill_ws<WS_CFG(_Float16, 3), 256, 128, WS_BK(3), 3, 4, 4>(info, M, N, K);
-      else if (s == 4) fill_ws<WS_CFG(_Float16, 4), 256, 128, WS_BK(4), 4, 4, 4>(info, M, N, K);
+      int s = stages == 0 ? kWsDefaultStages : stages;
+      if (s == 1) fill_nt<WsGeom<1>>(info, M, N, K);
+      else if (s == 2) fill_nt<WsGeom<2>>(info, M, N, K);
+      else if (s == 3) fill_nt<WsGeom<3>>(info, M, N, K);
+      else if (s == 4) fill_nt<WsGeom<4>>(info, M, N, K);
       else return PGEMM_ERR_STAGES;
       *stages_out = s;
       break;
@@ -175,34 +153,31 @@ pgemm_status check_ptrs(const void *lhs, const void *rhs, const void *out, int64
 
 pgemm_status launched() { return hipGetLastError() == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH; }
 
-template <typename T, int S>
+template <typename T, class G>
 pgemm_status launch_swap(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int M, int N, int K,
                          hipStream_t stream, int dev) {
-  using Cfg = SwapCfg<T, 256, 256, 64, S>;
-  auto kern = nt_swap_kernel<T, 256, 256, 64, S>;
+  auto kern = nt_swap_kernel<T, G>;
   static std::atomic<uint64_t> lds_set{0};
-  pgemm_status st = allow_lds(kern, Cfg::LDS_BYTES, dev, lds_set);
+  pgemm_status st = allow_lds(kern, G::LDS_BYTES, dev, lds_set);
   if (st != PGEMM_OK) return st;
-  const int tm = (int)cdiv(M, 256), tn = (int)cdiv(N, 256);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tm * (int64_t)tn)), dim3(Cfg::THREADS), Cfg::LDS_BYTES, stream, lhs,
-                     rhs, out, M, N, K, tm, tn, kGroupM);
+  const int tm = (int)cdiv(M, G::BM), tn = (int)cdiv(N, G::BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tm * (int64_t)tn)), dim3(G::THREADS), G::LDS_BYTES, stream, lhs, rhs,
+                     out, M, N, K, tm, tn, kGroupM);
   return launched();
 }
 
-template <typename T, int S>
+template <typename T, class G>
 pgemm_status launch_ws(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int M, int N, int K,
                        hipStream_t stream, int dev) {
-  constexpr int BK = WS_BK(S);
-  using Cfg = WsCfg<T, 256, 128, BK, S, 4, 4>;
-  auto kern = nt_ws_kernel<T, 256, 128, BK, S, 4, 4>;
+  auto kern = nt_ws_kernel<T, G>;
   static std::atomic<uint64_t> lds_set{0};
-  pgemm_status st = allow_lds(kern, Cfg::LDS_BYTES, dev, lds_set);
+  pgemm_status st = allow_lds(kern, G::LDS_BYTES, dev, lds_set);
   if (st != PGEMM_OK) return st;
-  const int tm = (int)cdiv(M, 256), tn = (int)cdiv(N, 128);
+  const int tm = (int)cdiv(M, G::BM), tn = (int)cdiv(N, G::BN);
   uint32_t polls = g_max_polls.load(std::memory_order_relaxed);
   int skip = g_skip_seed.load(std::memory_order_relaxed);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tm * (int64_t)tn)), dim3(Cfg::THREADS), Cfg::LDS_BYTES, stream, lhs, rhs,
-                     out, M, N, K, tm, tn, kGroupM, polls, skip, g_err_ptr[dev]);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tm * (int64_t)tn)), dim3(G::THREADS), G::LDS_BYTES, stream, lhs, rhs, out,
+                     M, N, K, tm, tn, kGroupM, polls, skip, g_err_ptr[dev]);
   return launched();
 }
 
@@ -224,15 +199,15 @@ pgemm_status nt_entry(pgemm_op op, const uint16_t *lhs, const uint16_t *rhs, uin
   const int m = (int)M, n = (int)N, k = (int)K;
   if (op == PGEMM_OP_NT_SWAP) {
     switch (s) {
-      case 1: return launch_swap<T, 1>(lhs, rhs, out, m, n, k, h, dev);
-      case 2: return launch_swap<T, 2>(lhs, rhs, out, m, n, k, h, dev);
+      case 1: return launch_swap<T, SwapGeom<1>>(lhs, rhs, out, m, n, k, h, dev);
+      case 2: return launch_swap<T, SwapGeom<2>>(lhs, rhs, out, m, n, k, h, dev);
     }
   } else {
     switch (s) {
-      case 1: return launch_ws<T, 1>(lhs, rhs, out, m, n, k, h, dev);
-      case 2: return launch_ws<T, 2>(lhs, rhs, out, m, n, k, h, dev);
-      case 3: return launch_ws<T, 3>(lhs, rhs, out, m, n, k, h, dev);
-      case 4: return launch_ws<T, 4>(lhs, rhs, out, m, n, k, h, dev);
+      case 1: return launch_ws<T, WsGeom<1>>(lhs, rhs, out, m, n, k, h, dev);
+      case 2: return launch_ws<T, WsGeom<2>>(lhs, rhs, out, m, n, k, h, dev);
+      case 3: return launch_ws<T, WsGeom<3>>(lhs, rhs, out, m, n, k, h, dev);
+      case 4: return launch_ws<T, WsGeom<4>>(lhs, rhs, out, m, n, k, h, dev);
     }
   }
   return PGEMM_ERR_STAGES;

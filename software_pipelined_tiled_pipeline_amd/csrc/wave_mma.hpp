@@ -79,13 +79,14 @@ struct WaveTile {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int p = ((2 * kk + hi) ^ s) * 16;
+      // rhs fragments first: the first MFMA needs bf[0] and af[0] only
       u32x4 af[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const u32x4 *>(a_lane + 32 * i * Row::ROW_BYTES + p);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         bf[j] = *reinterpret_cast<const u32x4 *>(b_lane + 32 * j * Row::ROW_BYTES + p);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const u32x4 *>(a_lane + 32 * i * Row::ROW_BYTES + p);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
