@@ -95,21 +95,34 @@ __device__ __forceinline__ void tile_of_block(int64_t bid, int64_t nblocks, int 
 // A wait polls with s_sleep between reads and gives up after `max_polls`
 // reads, recording the failure in *err (so a protocol error can never hang
 // the device).
-__device__ __forceinline__ uint32_t lds_load_relaxed(uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+//
+// The counter read and the increment are issued as inline assembly.  The
+// compiler treats every LDS access that follows a direct-to-LDS load as a
+// possible alias of it and would put `s_waitcnt vmcnt(0)` in front, i.e.
+// wait for every load in flight, which would undo the pipeline.  Ordering is
+// explicit instead: a producer waits for its own loads with a counted
+// `s_waitcnt vmcnt` before it triggers `full`; a consumer waits for its
+// fragment reads (`s_waitcnt lgkmcnt(0)`) before it triggers `empty`; and
+// LDS executes one wave's accesses in issue order.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+__device__ __forceinline__ uint32_t credit_peek(const uint32_t *ctr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(ctr)) : "memory");
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
 __device__ __forceinline__ void credit_trigger(uint32_t *ctr) {
-  compiler_fence();
   if ((threadIdx.x & (kWave - 1)) == 0)
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  compiler_fence();
+    asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(ctr)), "v"(1u) : "memory");
 }
 
-__device__ __forceinline__ void credit_wait(uint32_t *ctr, uint32_t target, uint32_t max_polls,
+__device__ __forceinline__ void credit_wait(const uint32_t *ctr, uint32_t target, uint32_t max_polls,
                                             uint32_t *err) {
   uint32_t polls = 0;
-  while (lds_load_relaxed(ctr) < target) {
+  while (credit_peek(ctr) < target) {
     if (++polls > max_polls) {
       if ((threadIdx.x & (kWave - 1)) == 0) atomicOr(err, 1u);
       break;

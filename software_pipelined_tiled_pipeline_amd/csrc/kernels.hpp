@@ -166,8 +166,13 @@ struct NtGeom {
   static constexpr int STAGE_BYTES = BM * Staging<BN>::PITCH;
   static constexpr int CTR_OFFSET = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
   static constexpr int LDS_BYTES = CTR_OFFSET + (P > 0 ? 2 * S * 4 : 0);
-  // a producer keeps up to S-1 tiles in flight before signalling the oldest
-  static constexpr int LAG = S - 1;
+  // Tiles a producer keeps in flight before it signals the oldest.  Issuing
+  // tile t needs the slot of tile t-S back from the consumers, so `full` for
+  // tile t-LAG is published only after the consumers have finished tile t-S.
+  // The consumers need tile t-LAG as soon as they finish tile t-LAG-1; with
+  // LAG <= S-2 that event lies at least one tile after the one the signal
+  // waits for, so the signal is never what holds the consumers up.
+  static constexpr int LAG = S >= 2 ? S - 2 : 0;
   static_assert(Loader::INSTR % LOADERS == 0, "loads split evenly");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave blocks are whole 32x32 MFMA tiles");
   static_assert(S <= 4, "vmcnt wait table covers three tiles in flight");
@@ -201,7 +206,8 @@ __global__ void __launch_bounds__(G::THREADS)
   auto slot_ptr = [&](int s) { return smem + s * Loader::SLOT_BYTES; };
   auto compute = [&](int s) {
     char *base = slot_ptr(s);
-    w.mma_ktile(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
+    w.template mma_ktile<true>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES,
+                               lane);
   };
   const int first = wave * G::PER_LOADER;
 
@@ -269,7 +275,8 @@ __global__ void __launch_bounds__(G::THREADS)
       const uint32_t round = (uint32_t)(t / S);
       credit_wait(&full[s], (uint32_t)P * (round + 1u), max_polls, err);
       char *base = slot_ptr(s);
-      w.mma_ktile(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
+      w.template mma_ktile<false>(base + wm * G::WM * Row::ROW_BYTES,
+                                  base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
       wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
       credit_trigger(&empty[s]);
     }

@@ -10,7 +10,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "../../include/pgemm.h"
+#include "pgemm.h"
 #include "instances.hpp"
 
 // Device-side error word: a credit wait that runs past its poll limit sets

@@ -67,30 +67,58 @@ struct WaveTile {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   }
 
+  // Fragments of one k16 step: TN rhs and TM lhs 16-byte pieces per lane.
+  struct Frags {
+    u32x4 b[TN], a[TM];
+  };
+
+  // Lane l reads row (base + l % 32) at chunk 2 kk + l / 32 of the K tile;
+  // `lane_a` / `lane_b` already point at that row of the wave's first block.
+  __device__ __forceinline__ static void read_frags(Frags &f, const char *lane_a, const char *lane_b, int kk,
+                                                    int hi, int s) {
+    const int p = ((2 * kk + hi) ^ s) * 16;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const u32x4 *>(lane_b + 32 * j * Row::ROW_BYTES + p);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const u32x4 *>(lane_a + 32 * i * Row::ROW_BYTES + p);
+  }
+
+  __device__ __forceinline__ void mma_step(const Frags &f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T>::run(f.b[j], f.a[i], acc[i][j]);
+  }
+
   // One K tile from a ring slot.  a_rows / b_rows: LDS address of the first
   // of this wave's lhs / rhs rows in the slot; both are multiples of 32 rows
-  // from the tile start, so the swizzle term depends on l % 32 only.
+  // from the tile start, so the swizzle term depends on l % 32 only.  With
+  // PREFETCH the fragments of step kk+1 are read while step kk's MFMAs run
+  // (two fragment sets live); without it one set is live and latency is left
+  // to the other waves of the SIMD.
+  template <bool PREFETCH>
   __device__ __forceinline__ void mma_ktile(const char *a_rows, const char *b_rows, int lane) {
     const int r = lane & 31;
     const int hi = lane >> 5;
     const int s = Row::swz(r);
-    const char *a_lane = a_rows + r * Row::ROW_BYTES;
-    const char *b_lane = b_rows + r * Row::ROW_BYTES;
+    const char *lane_a = a_rows + r * Row::ROW_BYTES;
+    const char *lane_b = b_rows + r * Row::ROW_BYTES;
+    constexpr int NK = BK / 16;
+    if constexpr (PREFETCH) {
+      Frags f[2];
+      read_frags(f[0], lane_a, lane_b, 0, hi, s);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int p = ((2 * kk + hi) ^ s) * 16;
-      // rhs fragments first: the first MFMA needs bf[0] and af[0] only
-      u32x4 af[TM], bf[TN];
+      for (int kk = 0; kk < NK; ++kk) {
+        if (kk + 1 < NK) read_frags(f[(kk + 1) & 1], lane_a, lane_b, kk + 1, hi, s);
+        mma_step(f[kk & 1]);
+      }
+    } else {
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bf[j] = *reinterpret_cast<const u32x4 *>(b_lane + 32 * j * Row::ROW_BYTES + p);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const u32x4 *>(a_lane + 32 * i * Row::ROW_BYTES + p);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T>::run(bf[j], af[i], acc[i][j]);
+      for (int kk = 0; kk < NK; ++kk) {
+        Frags f;
+        read_frags(f, lane_a, lane_b, kk, hi, s);
+        mma_step(f);
+      }
     }
   }
 
