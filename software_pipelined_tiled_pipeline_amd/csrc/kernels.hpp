@@ -130,6 +130,34 @@ struct SlotLoader {
       load_lds_x4(is_a ? ra : rb, slot + j * (kWave * 16), off);
     }
   }
+
+  // Register path, same granule map: `fetch` brings the 16 bytes that lane l
+  // of instruction j would write into registers, `put` writes them to the
+  // slot (lane l of instruction j -> granule 64 j + l, conflict-free).
+  template <int COUNT>
+  __device__ __forceinline__ void fetch(u32x4 (&r)[COUNT], int t, int first, int lane) const {
+    const int k0 = t * BK;
+    const bool whole = k0 + BK <= K;
+#pragma unroll
+    for (int i = 0; i < COUNT; ++i) {
+      const int j = first + i;
+      const bool is_a = j < A_INSTR;
+      const int jj = is_a ? j : j - A_INSTR;
+      const int row = jj * (kWave / CPR) + lane / CPR;
+      const int chunk = (lane % CPR) ^ Row::swz(row);
+      const int kc = k0 + chunk * 8;
+      uint32_t off = ((uint32_t)row * (uint32_t)K + (uint32_t)kc) * 2u;
+      if (!whole && kc >= K) off = kOobOffset;
+      r[i] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? ra : rb, (int)off, 0, 0);
+    }
+  }
+
+  template <int COUNT>
+  __device__ __forceinline__ static void put(const u32x4 (&r)[COUNT], char *slot, int first, int lane) {
+#pragma unroll
+    for (int i = 0; i < COUNT; ++i)
+      *reinterpret_cast<u32x4 *>(slot + (first + i) * (kWave * 16) + lane * 16) = r[i];
+  }
 };
 
 // vmcnt wait with a run-time count that is a multiple of STEP below 4*STEP.
@@ -166,13 +194,15 @@ struct NtGeom {
   static constexpr int STAGE_BYTES = BM * Staging<BN>::PITCH;
   static constexpr int CTR_OFFSET = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
   static constexpr int LDS_BYTES = CTR_OFFSET + (P > 0 ? 2 * S * 4 : 0);
-  // Tiles a producer keeps in flight before it signals the oldest.  Issuing
-  // tile t needs the slot of tile t-S back from the consumers, so `full` for
-  // tile t-LAG is published only after the consumers have finished tile t-S.
-  // The consumers need tile t-LAG as soon as they finish tile t-LAG-1; with
-  // LAG <= S-2 that event lies at least one tile after the one the signal
-  // waits for, so the signal is never what holds the consumers up.
-  static constexpr int LAG = S >= 2 ? S - 2 : 0;
+  // Producer register staging: each producer wave holds its share of the
+  // next RBUF K tiles in VGPRs (global -> VGPR while the tile's ring slot is
+  // still being read, VGPR -> LDS once the slot's `empty` credit arrives).
+  // Every wave of the kernel is allocated the consumers' register budget
+  // anyway, so these buffers cost nothing and add RBUF tiles of loads in
+  // flight beyond what the LDS ring holds.
+  static constexpr int RBUF = P > 0 ? (BK == 64 ? 2 : 4) : 0;
+  static_assert(P == 0 || RBUF * PER_LOADER * 4 <= 128, "staging fits the producer's registers");
+  static_assert(P == 0 || RBUF * PER_LOADER < 64, "staged loads fit the 6-bit vmcnt");
   static_assert(Loader::INSTR % LOADERS == 0, "loads split evenly");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave blocks are whole 32x32 MFMA tiles");
   static_assert(S <= 4, "vmcnt wait table covers three tiles in flight");
@@ -285,19 +315,24 @@ __global__ void __launch_bounds__(G::THREADS)
     Loader ld;
     ld.init(lhs, rhs, M, N, K, m0, n0);
     const int first = (wave - C) * G::PER_LOADER;
-    for (int t = 0; t < n_k; ++t) {
-      const int s = t % S;
-      const uint32_t round = (uint32_t)(t / S);
-      credit_wait(&empty[s], (uint32_t)C * (round + 1u), max_polls, err);
-      ld.template load<G::PER_LOADER>(slot_ptr(s), t, first, lane);
-      if (t >= G::LAG) {
-        wait_vmcnt_steps<G::PER_LOADER>(G::LAG);  // tile t-LAG has landed
-        credit_trigger(&full[(t - G::LAG) % S]);
+    constexpr int R = G::RBUF;
+    u32x4 buf[R][G::PER_LOADER];
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (j < n_k) ld.fetch(buf[j], j, first, lane);  // prologue: R tiles in flight
+    for (int t0 = 0; t0 < n_k; t0 += R) {
+#pragma unroll
+      for (int b = 0; b < R; ++b) {
+        const int t = t0 + b;
+        if (t >= n_k) break;
+        const int s = t % S;
+        const uint32_t round = (uint32_t)(t / S);
+        credit_wait(&empty[s], (uint32_t)C * (round + 1u), max_polls, err);  // slot free
+        Loader::put(buf[b], slot_ptr(s), first, lane);  // waits for tile t's loads only
+        wait_lgkmcnt0();                                 // the slot holds tile t
+        credit_trigger(&full[s]);
+        if (t + R < n_k) ld.fetch(buf[b], t + R, first, lane);  // refill the register stage
       }
-    }
-    for (int t = n_k - G::LAG < 0 ? 0 : n_k - G::LAG; t < n_k; ++t) {  // drain
-      wait_vmcnt_steps<G::PER_LOADER>(n_k - 1 - t);
-      credit_trigger(&full[t % S]);
     }
   }
   __syncthreads();  // all tiles consumed: the ring becomes the staging tile
