@@ -5,10 +5,11 @@
 
 namespace pgemm {
 
-// Single schedule: 256 x 256 output tile, eight waves (two per SIMD) of
-// 128 x 64, K tile 64; the ring holds one or two 64 KiB slots.
+// Single schedule: 256 x 256 output tile, four waves (one per SIMD, up to
+// 512 registers each) of 128 x 128, K tile 64; the ring holds one or two
+// 64 KiB slots.
 template <int S>
-using SwapGeom = NtGeom<256, 256, 64, S, 2, 4, 0>;
+using SwapGeom = NtGeom<256, 256, 64, S, 2, 2, 0>;
 
 // Producer/consumer: 256 x 256 output tile, eight consumer waves of
 // 128 x 64 (two per SIMD) and four producer waves (one per SIMD), so every

@@ -211,14 +211,34 @@ struct NtGeom {
 
 // ======================================================= NT, single schedule
 
+// Every wave fills its share of the ring with direct-to-LDS loads and runs
+// MFMA on its own block; one workgroup barrier per K tile.  The fragments of
+// k16 step kk+1 are read while step kk's MFMAs run (two fragment sets), and
+// the barrier sits at the start of a tile's last step rather than at the
+// tile boundary, so the stream of MFMAs does not stop at tiles:
+//
+//   barrier before the last step of tile t:
+//     - each wave first waits for its own loads of tile t+1 (RAW: tile t+1
+//       is complete once every wave has passed);
+//     - every read of tile t has been issued and drained (WAR: tile t's slot
+//       is free once every wave has passed);
+//   after it: loads of tile t+S into tile t's slot are issued, the first
+//   fragments of tile t+1 are read, and tile t's last MFMAs run.
+//
+// The loads of a tile are issued S-1 tiles ahead (at the barrier in tile
+// t-S, when its slot comes free).  S = 1
+// has a single slot and runs fill -> barrier -> compute -> barrier.
 template <typename T, class G>
-__global__ void __launch_bounds__(G::THREADS)
+__global__ void __launch_bounds__(G::THREADS, 1)
     nt_swap_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
                    uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m) {
   static_assert(G::P == 0, "single-schedule kernel has no producer waves");
   using Loader = typename G::Loader;
   using Row = RingRow<G::BK>;
+  using W = WaveTile<T, G::WM, G::WN, G::BK>;
   constexpr int S = G::S;
+  constexpr int NK = G::BK / 16;
+  static_assert(NK % 2 == 0, "fragment sets alternate per step and must line up per tile");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -230,35 +250,55 @@ __global__ void __launch_bounds__(G::THREADS)
 
   Loader ld;
   ld.init(lhs, rhs, M, N, K, m0, n0);
-  WaveTile<T, G::WM, G::WN, G::BK> w;
+  W w;
   w.zero();
   const int n_k = (K + G::BK - 1) / G::BK;
   auto slot_ptr = [&](int s) { return smem + s * Loader::SLOT_BYTES; };
-  auto compute = [&](int s) {
-    char *base = slot_ptr(s);
-    w.template mma_ktile<true>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES,
-                               lane);
-  };
   const int first = wave * G::PER_LOADER;
+  const int r = lane & 31, hi = lane >> 5, sw = Row::swz(r);
+  auto lane_a = [&](int s) { return slot_ptr(s) + (wm * G::WM + r) * Row::ROW_BYTES; };
+  auto lane_b = [&](int s) { return slot_ptr(s) + (G::BM + wn * G::WN + r) * Row::ROW_BYTES; };
 
   if constexpr (S == 1) {
+    typename W::Frags f;
     for (int t = 0; t < n_k; ++t) {
       ld.template load<G::PER_LOADER>(slot_ptr(0), t, first, lane);
       wait_vmcnt<0>();
       lds_barrier();
-      compute(0);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        W::read_frags(f, lane_a(0), lane_b(0), kk, hi, sw);
+        w.mma_step(f);
+      }
       lds_barrier();
     }
   } else {
-    // prologue: tiles 0 .. S-2 in flight
-    for (int j = 0; j < S - 1 && j < n_k; ++j) ld.template load<G::PER_LOADER>(slot_ptr(j), j, first, lane);
+    typename W::Frags f[2];
+    // prologue: tiles 0 .. S-1 in flight (one per slot), tile 0 landed, its
+    // first fragments read
+    for (int j = 0; j < S && j < n_k; ++j) ld.template load<G::PER_LOADER>(slot_ptr(j), j, first, lane);
+    if (n_k > 0) {
+      wait_vmcnt_steps<G::PER_LOADER>((n_k - 1) < (S - 1) ? (n_k - 1) : (S - 1));
+      lds_barrier();
+      W::read_frags(f[0], lane_a(0), lane_b(0), 0, hi, sw);
+    }
     for (int t = 0; t < n_k; ++t) {
-      // tile t has landed once at most min(S-2, n_k-1-t) younger tiles are pending
-      const int younger = (n_k - 1 - t) < (S - 2) ? (n_k - 1 - t) : (S - 2);
-      wait_vmcnt_steps<G::PER_LOADER>(younger);
-      lds_barrier();  // tile t visible to all; everyone is done with tile t-1
-      if (t + S - 1 < n_k) ld.template load<G::PER_LOADER>(slot_ptr((t + S - 1) % S), t + S - 1, first, lane);
-      compute(t % S);
+      const int s = t % S;
+#pragma unroll
+      for (int kk = 0; kk + 1 < NK; ++kk) {
+        W::read_frags(f[(kk + 1) & 1], lane_a(s), lane_b(s), kk + 1, hi, sw);
+        w.mma_step(f[kk & 1]);
+      }
+      if (t + 1 < n_k) {
+        // tile t+1 complete once every wave has waited for its own share;
+        // loads still allowed in flight: those of tiles t+2 .. t+S-1
+        const int younger = (n_k - 2 - t) < (S - 2) ? (n_k - 2 - t) : (S - 2);
+        wait_vmcnt_steps<G::PER_LOADER>(younger);
+        lds_barrier();
+        if (t + S < n_k) ld.template load<G::PER_LOADER>(slot_ptr(s), t + S, first, lane);
+        W::read_frags(f[0], lane_a((t + 1) % S), lane_b((t + 1) % S), 0, hi, sw);
+      }
+      w.mma_step(f[(NK - 1) & 1]);
     }
   }
   __syncthreads();  // ring no longer read: reuse it as the staging tile

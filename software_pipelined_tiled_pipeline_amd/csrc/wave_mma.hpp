@@ -74,6 +74,8 @@ struct WaveTile {
 
   // Lane l reads row (base + l % 32) at chunk 2 kk + l / 32 of the K tile;
   // `lane_a` / `lane_b` already point at that row of the wave's first block.
+  // `lane_a` / `lane_b` point at the lane's row of the wave's first lhs /
+  // rhs block in a slot; s = swz(l % 32).
   __device__ __forceinline__ static void read_frags(Frags &f, const char *lane_a, const char *lane_b, int kk,
                                                     int hi, int s) {
     const int p = ((2 * kk + hi) ^ s) * 16;
