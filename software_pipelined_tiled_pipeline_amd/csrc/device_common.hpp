@@ -35,9 +35,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 
 // One wave-wide direct-to-LDS load: lane l copies 16 bytes from
-// rsrc + voffset(l) to lds_dst + 16 * l.  `lds_dst` must be wave-uniform.
-__device__ __forceinline__ void load_lds_x4(__amdgpu_buffer_rsrc_t rsrc, char *lds_dst, uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds_dst, 16, voffset, 0, 0, 0);
+// rsrc + voffset(l) + soffset to lds_dst + 16 * l.  `lds_dst` and `soffset`
+// must be wave-uniform.  Out-of-range reads return zero.  Callers keep the
+// row part of an offset in voffset and only the K offset in soffset, and
+// send a lane whose chunk lies past K to kOobOffset: then a lane reads zero
+// exactly when its element is outside the matrix, whether or not the
+// hardware adds soffset before the bound check.
+__device__ __forceinline__ void load_lds_x4(__amdgpu_buffer_rsrc_t rsrc, char *lds_dst, uint32_t voffset,
+                                            uint32_t soffset = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds_dst, 16, voffset, soffset, 0, 0);
 }
 
 template <int N>

@@ -16,6 +16,8 @@
 // later needs S versions).
 #pragma once
 
+#include <type_traits>
+
 #include "wave_mma.hpp"
 
 namespace pgemm {
@@ -99,10 +101,18 @@ struct SlotLoader {
   static constexpr int A_INSTR = BM * CPR / kWave;
   static constexpr int INSTR = (BM + BN) * CPR / kWave;
   static constexpr int SLOT_BYTES = (BM + BN) * Row::ROW_BYTES;
+  static constexpr int RPI = kWave / CPR;  // rows per instruction
+  // Within instruction jj (of the A or the B tile), lane l covers row
+  // jj * RPI + l / CPR; its swizzle is (4 jj + l / 16) mod CPR, so the lane's
+  // chunk depends on jj only through jj mod PAR.
+  static constexpr int PAR = CPR / 4;
+  static_assert(A_INSTR % PAR == 0, "instruction parity is the same in both tiles");
   static_assert((BM * CPR) % kWave == 0 && (BN * CPR) % kWave == 0, "tiles fill whole instructions");
 
   __amdgpu_buffer_rsrc_t ra, rb;
   int K;
+  uint32_t lane_off[PAR];  // (l / CPR) * row bytes + chunk * 16, per parity
+  int lane_k[PAR];         // chunk * 8: the lane's first k within the tile
 
   __device__ __forceinline__ void init(const uint16_t *lhs, const uint16_t *rhs, int M, int N, int K_,
                                        int m0, int n0) {
@@ -111,24 +121,34 @@ struct SlotLoader {
     const int rows_b = N - n0 < BN ? N - n0 : BN;
     ra = make_rsrc(lhs + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K * 2u);
     rb = make_rsrc(rhs + (int64_t)n0 * K, (uint32_t)rows_b * (uint32_t)K * 2u);
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int p = 0; p < PAR; ++p) {
+      const int chunk = (lane % CPR) ^ ((4 * p + lane / 16) % CPR);
+      lane_off[p] = (uint32_t)(lane / CPR) * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
+      lane_k[p] = chunk * 8;
+    }
   }
 
+  // Instruction j of the slot for K tile t (lane l -> granule 64 j + l);
+  // p = j mod PAR, passed as a constant (every caller's first instruction is
+  // a multiple of PAR, as is A_INSTR) so that the per-lane arrays stay in
+  // registers.
+  __device__ __forceinline__ void load_one(char *slot, int t, int j, int p) const {
+    const bool is_a = j < A_INSTR;
+    const int jj = is_a ? j : j - A_INSTR;
+    const int k0 = t * BK;
+    uint32_t voff = lane_off[p] + (uint32_t)(jj * RPI) * (uint32_t)K * 2u;
+    if (lane_k[p] >= K - k0) voff = kOobOffset;  // chunk past K (every lane, past the last tile)
+    load_lds_x4(is_a ? ra : rb, slot + j * (kWave * 16), voff, (uint32_t)k0 * 2u);
+  }
+
+  // Instructions first .. first+COUNT-1 of the slot for tile t.
   template <int COUNT>
   __device__ __forceinline__ void load(char *slot, int t, int first, int lane) const {
-    const int k0 = t * BK;
-    const bool whole = k0 + BK <= K;
+    (void)lane;
 #pragma unroll
-    for (int i = 0; i < COUNT; ++i) {
-      const int j = first + i;  // wave-uniform
-      const bool is_a = j < A_INSTR;
-      const int jj = is_a ? j : j - A_INSTR;
-      const int row = jj * (kWave / CPR) + lane / CPR;
-      const int chunk = (lane % CPR) ^ Row::swz(row);
-      const int kc = k0 + chunk * 8;
-      uint32_t off = ((uint32_t)row * (uint32_t)K + (uint32_t)kc) * 2u;
-      if (!whole && kc >= K) off = kOobOffset;
-      load_lds_x4(is_a ? ra : rb, slot + j * (kWave * 16), off);
-    }
+    for (int i = 0; i < COUNT; ++i) load_one(slot, t, first + i, i % PAR);
   }
 
   // Register path, same granule map: `fetch` brings the 16 bytes that lane l
@@ -158,6 +178,19 @@ struct SlotLoader {
     for (int i = 0; i < COUNT; ++i)
       *reinterpret_cast<u32x4 *>(slot + (first + i) * (kWave * 16) + lane * 16) = r[i];
   }
+};
+
+// Load issuers for mixed_step: call i issues instruction first + i of the
+// slot for `tile` (first is a multiple of the loader's parity period).
+template <class Loader>
+struct RefillLoads {
+  Loader ld;
+  char *slot;
+  int tile, first;
+  __device__ __forceinline__ void operator()(int i) const { ld.load_one(slot, tile, first + i, i % Loader::PAR); }
+};
+struct NoLoads {
+  __device__ __forceinline__ void operator()(int) const {}
 };
 
 // vmcnt wait with a run-time count that is a multiple of STEP below 4*STEP.
@@ -273,32 +306,50 @@ __global__ void __launch_bounds__(G::THREADS, 1)
       lds_barrier();
     }
   } else {
+    // A slot freed at the barrier of tile t is refilled with tile t+S: half
+    // of this wave's loads during tile t's last step, half during the first
+    // step of tile t+1, each spread out between MFMAs (see mixed_step).  The
+    // prologue issues tiles 0 .. S-2 and the first half of tile S-1, so the
+    // steady state starts as if a refill were under way.  Loads of tiles at
+    // or past the end read only out-of-range offsets (zeros into slots no
+    // later tile uses); issuing them anyway keeps every vmcnt target static.
+    constexpr int PER = G::PER_LOADER;
+    constexpr int HALF = PER / 2;
+    static_assert(PER % 2 == 0 && HALF % Loader::PAR == 0, "refill loads split in halves");
     typename W::Frags f[2];
-    // prologue: tiles 0 .. S-1 in flight (one per slot), tile 0 landed, its
-    // first fragments read
-    for (int j = 0; j < S && j < n_k; ++j) ld.template load<G::PER_LOADER>(slot_ptr(j), j, first, lane);
-    if (n_k > 0) {
-      wait_vmcnt_steps<G::PER_LOADER>((n_k - 1) < (S - 1) ? (n_k - 1) : (S - 1));
-      lds_barrier();
-      W::read_frags(f[0], lane_a(0), lane_b(0), 0, hi, sw);
-    }
-    for (int t = 0; t < n_k; ++t) {
+    NoLoads no_load;
+    for (int j = 0; j + 1 < S; ++j) ld.template load<PER>(slot_ptr(j), j, first, lane);
+    ld.template load<HALF>(slot_ptr(S - 1), S - 1, first, lane);
+    wait_vmcnt<(S - 2) * PER + HALF>();  // tile 0 landed
+    lds_barrier();
+    if (n_k > 0) W::read_frags(f[0], lane_a(0), lane_b(0), 0, hi, sw);
+    int refill = S - 1, rslot = S - 1;
+    // steps 0 .. NK-2 of tile t (step 0 carries the second half of the refill)
+    auto head = [&](int t) __attribute__((always_inline)) {
       const int s = t % S;
+      w.template mixed_step<true, HALF>(f[0], f[1], lane_a(s), lane_b(s), 1, hi, sw,
+                                        RefillLoads<Loader>{ld, slot_ptr(rslot), refill, first + HALF});
 #pragma unroll
-      for (int kk = 0; kk + 1 < NK; ++kk) {
-        W::read_frags(f[(kk + 1) & 1], lane_a(s), lane_b(s), kk + 1, hi, sw);
-        w.mma_step(f[kk & 1]);
-      }
-      if (t + 1 < n_k) {
-        // tile t+1 complete once every wave has waited for its own share;
-        // loads still allowed in flight: those of tiles t+2 .. t+S-1
-        const int younger = (n_k - 2 - t) < (S - 2) ? (n_k - 2 - t) : (S - 2);
-        wait_vmcnt_steps<G::PER_LOADER>(younger);
-        lds_barrier();
-        if (t + S < n_k) ld.template load<G::PER_LOADER>(slot_ptr(s), t + S, first, lane);
-        W::read_frags(f[0], lane_a((t + 1) % S), lane_b((t + 1) % S), 0, hi, sw);
-      }
-      w.mma_step(f[(NK - 1) & 1]);
+      for (int kk = 1; kk + 1 < NK; ++kk)
+        w.template mixed_step<true, 0>(f[kk & 1], f[(kk + 1) & 1], lane_a(s), lane_b(s), kk + 1, hi, sw, no_load);
+    };
+    // (the last tile is peeled off so that the loop body has one path)
+    for (int t = 0; t + 1 < n_k; ++t) {
+      const int s = t % S;
+      head(t);
+      // tile t+1 complete once every wave has waited for its own share;
+      // still in flight after it: tiles t+2 .. t+S-1
+      wait_vmcnt<(S - 2) * PER>();
+      lds_barrier();
+      refill = t + S;  // into tile t's slot, now free
+      rslot = s;
+      const int s1 = (t + 1) % S;
+      w.template mixed_step<true, HALF>(f[1], f[0], lane_a(s1), lane_b(s1), 0, hi, sw,
+                                        RefillLoads<Loader>{ld, slot_ptr(s), t + S, first});
+    }
+    if (n_k > 0) {
+      head(n_k - 1);
+      w.template mixed_step<false, 0>(f[1], f[0], lane_a(0), lane_b(0), 0, hi, sw, no_load);
     }
   }
   __syncthreads();  // ring no longer read: reuse it as the staging tile

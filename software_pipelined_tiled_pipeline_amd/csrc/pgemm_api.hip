@@ -74,6 +74,8 @@ pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, pgem
       int s = stages == 0 ? kSwapDefaultStages : stages;
       if (s == 1) fill_nt<SwapGeom<1>>(info, M, N, K);
       else if (s == 2) fill_nt<SwapGeom<2>>(info, M, N, K);
+      else if (s == 3) fill_nt<SwapGeom<3>>(info, M, N, K);
+      else if (s == 4) fill_nt<SwapGeom<4>>(info, M, N, K);
       else return PGEMM_ERR_STAGES;
       *stages_out = s;
       break;
@@ -201,6 +203,8 @@ pgemm_status nt_entry(pgemm_op op, const uint16_t *lhs, const uint16_t *rhs, uin
     switch (s) {
       case 1: return launch_swap<T, SwapGeom<1>>(lhs, rhs, out, m, n, k, h, dev);
       case 2: return launch_swap<T, SwapGeom<2>>(lhs, rhs, out, m, n, k, h, dev);
+      case 3: return launch_swap<T, SwapGeom<3>>(lhs, rhs, out, m, n, k, h, dev);
+      case 4: return launch_swap<T, SwapGeom<4>>(lhs, rhs, out, m, n, k, h, dev);
     }
   } else {
     switch (s) {

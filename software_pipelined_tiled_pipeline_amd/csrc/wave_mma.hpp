@@ -124,6 +124,45 @@ struct WaveTile {
     }
   }
 
+  // One k16 step: the TM*TN MFMAs on `cf`, with, in a fixed interleave
+  // (one read every TM*TN/(TM+TN) MFMAs, one load every TM*TN/NLOAD), the
+  // fragment reads of the next step into `nf` when READS and NLOAD calls
+  // ld_fn(0 .. NLOAD-1).  sched_barrier(0) after every MFMA pins the order:
+  // global loads spaced out between MFMAs never pile up in the
+  // texture-address queue, where a full queue would stall the wave's
+  // in-order issue, MFMAs included.
+  template <bool READS, int NLOAD, class LoadFn>
+  __device__ __forceinline__ void mixed_step(const Frags &cf, Frags &nf, const char *lane_a, const char *lane_b,
+                                             int nkk, int hi, int s, LoadFn &&ld_fn) {
+    constexpr int NM = TM * TN;
+    constexpr int NR = TM + TN;
+    static_assert(NM % NR == 0 || !READS, "reads spread evenly");
+    static_assert(NLOAD == 0 || NM % NLOAD == 0, "loads spread evenly");
+    constexpr int RE = NM / NR;                         // MFMAs per read
+    constexpr int LE = NLOAD > 0 ? NM / NLOAD : NM + 1;  // MFMAs per load
+    const int p = ((2 * nkk + hi) ^ s) * 16;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int m = i * TN + j;
+        acc[i][j] = Mfma<T>::run(cf.b[j], cf.a[i], acc[i][j]);
+        if constexpr (READS) {
+          if (m % RE == RE - 1) {
+            const int r = m / RE;
+            if (r < TN)
+              nf.b[r] = *reinterpret_cast<const u32x4 *>(lane_b + 32 * r * Row::ROW_BYTES + p);
+            else
+              nf.a[r - TN] = *reinterpret_cast<const u32x4 *>(lane_a + 32 * (r - TN) * Row::ROW_BYTES + p);
+          }
+        }
+        if constexpr (NLOAD > 0) {
+          if (m % LE == LE - 1) ld_fn(m / LE);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+
   // Rounds the accumulators to T and writes them into an LDS staging tile
   // (row pitch `pitch` bytes) at this wave's (row0, col0).
   __device__ __forceinline__ void stage(char *st, int pitch, int row0, int col0, int lane) const {

@@ -61,7 +61,7 @@ def test_query_geometry(L):
     assert pgemm.pgemm_query("nt_ws", 0, 64, 64, 64)["stages"] == 4
 
 
-@pytest.mark.parametrize("op,stages", [("s32_nn", 3), ("nt_swap", 3), ("nt_ws", 5), ("nt_ws", -1)])
+@pytest.mark.parametrize("op,stages", [("s32_nn", 3), ("nt_swap", 5), ("nt_ws", 5), ("nt_ws", -1)])
 def test_query_rejects_stages(L, op, stages):
     info = pgemm.KernelInfo()
     assert L.pgemm_query(pgemm.OPS[op], stages, 64, 64, 64, ctypes.byref(info)) == ERR_STAGES

@@ -51,7 +51,7 @@ def assert_within_bound(fmt, got, ref, mag, what):
     return worst
 
 
-VARIANTS = [("swap", 1), ("swap", 2), ("ws", 1), ("ws", 2), ("ws", 3), ("ws", 4)]
+VARIANTS = [("swap", 1), ("swap", 2), ("swap", 3), ("swap", 4), ("ws", 1), ("ws", 2), ("ws", 3), ("ws", 4)]
 
 
 # ------------------------------------------------------------------ int32
@@ -185,14 +185,14 @@ def test_workload_f16_8192_stage_sweep(pg):
     A, B = inputs.make_operands("f16_nt", 8192, 8192, 8192, inputs.workload_seed(3))
     dA, dB = dev_half(A, "f16"), dev_half(B, "f16")
     outs = {f"ws S={s}": run_nt(pg, "f16", "ws", A, B, s, dA, dB) for s in (1, 2, 3, 4)}
-    outs["swap S=2"] = run_nt(pg, "f16", "swap", A, B, 2, dA, dB)
+    outs.update({f"swap S={s}": run_nt(pg, "f16", "swap", A, B, s, dA, dB) for s in (1, 2, 3, 4)})
     check_sampled("f16", A, B, outs, 3, count=1024)
     first = outs["ws S=1"]
     for k, v in outs.items():
         assert np.array_equal(v, first), f"{k} differs in bits from ws S=1"
 
 
-@pytest.mark.parametrize("variant,stages", [("ws", 4), ("ws", 2), ("swap", 2), ("swap", 1)])
+@pytest.mark.parametrize("variant,stages", [("ws", 4), ("ws", 2), ("swap", 4), ("swap", 2), ("swap", 1)])
 def test_workload_bf16_ragged_4095x1000x1000(pg, variant, stages):
     M, N, K = 4095, 1000, 1000
     A, B = inputs.make_operands("bf16_nt", M, N, K, inputs.workload_seed(4))
