@@ -133,7 +133,7 @@ def main():
 
     fns = {"ws": pgemm.pgemm_f16_nt_ws, "swap": pgemm.pgemm_f16_nt}
     sweep = {}
-    for variant, stage_set in (("ws", (1, 2, 3, 4)), ("swap", (1, 2))):
+    for variant, stage_set in (("ws", (1, 2, 3, 4)), ("swap", (1, 2, 3, 4))):
         for s in stage_set:
             f = fns[variant]
             call = lambda f=f, s=s: f(dA, dB, out=out, stages=s)

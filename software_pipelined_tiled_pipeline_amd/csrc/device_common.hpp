@@ -46,13 +46,17 @@ __device__ __forceinline__ void load_lds_x4(__amdgpu_buffer_rsrc_t rsrc, char *l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds_dst, 16, voffset, soffset, 0, 0);
 }
 
+// s_waitcnt through the builtin, so that the compiler's own wait insertion
+// sees it and does not add a stricter one after it.  gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8; an all-ones field
+// means "do not wait on this counter".
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 

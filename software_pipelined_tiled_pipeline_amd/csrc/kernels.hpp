@@ -193,17 +193,11 @@ struct NoLoads {
   __device__ __forceinline__ void operator()(int) const {}
 };
 
-// vmcnt wait with a run-time count that is a multiple of STEP below 4*STEP.
-template <int STEP>
-__device__ __forceinline__ void wait_vmcnt_steps(int steps) {
-  if (steps <= 0) wait_vmcnt<0>();
-  else if (steps == 1) wait_vmcnt<STEP < 64 ? STEP : 63>();
-  else if (steps == 2) wait_vmcnt<2 * STEP < 64 ? 2 * STEP : 63>();
-  else wait_vmcnt<3 * STEP < 64 ? 3 * STEP : 63>();
-}
-
 // Workgroup barrier that also orders this wave's LDS accesses before it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void lds_barrier() {
+  wait_lgkmcnt0();
+  __builtin_amdgcn_s_barrier();
+}
 
 template <int BN>
 struct Staging {

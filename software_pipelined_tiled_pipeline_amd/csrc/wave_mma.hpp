@@ -201,8 +201,9 @@ __device__ __forceinline__ void store_staged(const char *st, int pitch, uint16_t
     if (vec_ok && gn + 8 <= N) {
       *reinterpret_cast<u32x4 *>(dst) = v;
     } else {
-      const uint16_t *e = reinterpret_cast<const uint16_t *>(&v);
-      for (int x = 0; x < 8 && gn + x < N; ++x) dst[x] = e[x];
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        if (gn + x < N) dst[x] = (uint16_t)(v[x / 2] >> (16 * (x % 2)));
     }
   }
 }
