@@ -2,8 +2,8 @@
  * pgemm: software-pipelined tiled GEMM for AMD Instinct MI355X (gfx950).
  *
  * Plain C interface: host or device pointers and sizes only, no HIP or torch
- * types.  Every GEMM call enqueues one kernel on the caller's HIP stream and
- * returns without waiting for it.
+ * types.  Every GEMM call enqueues one kernel (two for a K-split product)
+ * on the caller's HIP stream and returns without waiting for it.
  *
  * Operation (Croqtile tutorial ch.6, "Synchronization: pipelines, events and
  * double buffering": the int32 listing with swap and the f16 1P1C listing
@@ -24,7 +24,8 @@
  *   - stream: a hipStream_t passed as void*; NULL is the null stream.
  *   - Errors in the arguments are reported before any HIP call is made, and
  *     nothing is enqueued.  PGEMM_ERR_LAUNCH reports a failed launch.
- *   - Calls are stateless and may be made concurrently on different streams.
+ *   - Calls may be made concurrently on different streams: the only state a
+ *     call touches is the K-split workspace, which is per (device, stream).
  */
 #ifndef PGEMM_H
 #define PGEMM_H
@@ -35,18 +36,19 @@
 extern "C" {
 #endif
 
-#define PGEMM_ABI_VERSION 1
+#define PGEMM_ABI_VERSION 2
 
 typedef enum {
   PGEMM_OK = 0,
   PGEMM_ERR_NULL = 1,    /* a required pointer is NULL                       */
-  PGEMM_ERR_SHAPE = 2,   /* negative or too large M, N, K                    */
+  PGEMM_ERR_SHAPE = 2,   /* negative or too large M, N, K; bad tiling request */
   PGEMM_ERR_STAGES = 3,  /* stages outside the set the entry point supports  */
   PGEMM_ERR_ALIGN = 4,   /* a pointer is not 16-byte aligned                 */
   PGEMM_ERR_LDS = 5,     /* the tile ring for these stages exceeds LDS       */
   PGEMM_ERR_LAUNCH = 6,  /* the HIP launch (or a HIP query) failed           */
   PGEMM_ERR_TIMEOUT = 7, /* a credit wait exceeded its poll limit            */
-  PGEMM_ERR_DEVICE = 8   /* the current device is not gfx950                 */
+  PGEMM_ERR_DEVICE = 8,  /* the current device is not gfx950                 */
+  PGEMM_ERR_NOMEM = 9    /* the K-split workspace could not be allocated      */
 } pgemm_status;
 
 /* Variant codes used by the query functions. */
@@ -70,13 +72,27 @@ pgemm_status pgemm_s32_nn(const int32_t *lhs, const int32_t *rhs, int32_t *out,
                           int64_t M, int64_t N, int64_t K, int stages, void *stream);
 
 /*
- * f16 NT GEMM, single-schedule variant: every wavefront both fills the next
- * ring slot and runs MFMA on the current one, one workgroup barrier per K
- * tile (Croqtile ch.6, swap double buffering, applied to the f16 kernel).
+ * f16 NT GEMM, single-schedule variant: every wavefront both fills ring
+ * slots and runs MFMA, one workgroup barrier per K tile (Croqtile ch.6,
+ * swap double buffering applied to the f16 kernel; with more than two slots
+ * the handles rotate instead of swapping).
  *   lhs: IEEE binary16 bits [M, K], rhs: binary16 bits [N, K] (row n of rhs
  *   is column n of the right operand), out: binary16 bits [M, N].
+ *   K must be a multiple of 8 (else PGEMM_ERR_ALIGN) and below 2^22.
  *   Products are exact and accumulate in fp32 in increasing k; the output is
- *   rounded to nearest-even.  stages: 1 or 2 (default 2).
+ *   rounded to nearest-even.  stages: 1..4 (default 2).
+ *
+ * Tiling (every NT call): the host plans 256 x 256 output tiles when they
+ * alone nearly fill the 256 CUs, else 128 x 128 tiles; a product that then
+ * still leaves half the CUs idle and has K >= 1024 is split along K into
+ * up to 16 pieces (multiples of 64), each workgroup computing one tile over
+ * one piece into an fp32 workspace, and a second kernel adds the pieces in
+ * increasing order and rounds.  The workspace is allocated by the library
+ * on first need, one per (device, stream), grown when a larger one is
+ * needed (after synchronising that stream) and kept until the process ends;
+ * PGEMM_ERR_NOMEM if it cannot be allocated.  pgemm_query reports the plan.
+ * For a given plan the result is deterministic; different plans (tile size,
+ * K split) may differ in the last bits.
  */
 pgemm_status pgemm_f16_nt(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out,
                           int64_t M, int64_t N, int64_t K, int stages, void *stream);
@@ -87,8 +103,9 @@ pgemm_status pgemm_f16_nt(const uint16_t *lhs, const uint16_t *rhs, uint16_t *ou
  * ring slot t mod stages after waiting for its `empty` credit and then
  * signal `full`; consumer wavefronts seed one `empty` credit per slot before
  * the K loop, wait for `full`, run MFMA and return `empty`.  The credits are
- * monotonic counters in LDS.  Same layouts and numerics as pgemm_f16_nt; for
- * the same shape both give bit-identical results.  stages: 1..4 (default 4).
+ * monotonic counters in LDS.  Same layouts, rules, tiling and numerics as
+ * pgemm_f16_nt; for the same plan both give bit-identical results.
+ * stages: 1..4 (default 4).
  */
 pgemm_status pgemm_f16_nt_ws(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out,
                              int64_t M, int64_t N, int64_t K, int stages, void *stream);
@@ -113,8 +130,11 @@ typedef struct {
   int32_t consumer_waves;            /* waves running the math             */
   int32_t threads;                   /* threads per workgroup              */
   int32_t lds_bytes;                 /* LDS per workgroup                  */
-  int64_t grid;                      /* workgroups launched                */
-  int64_t k_tiles;                   /* cdiv(K, block_k)                   */
+  int64_t grid;                      /* workgroups launched (all pieces)   */
+  int64_t k_tiles;                   /* K tiles per workgroup (per piece)  */
+  int32_t k_split;                   /* K pieces; 1 = no split             */
+  int32_t reserved;                  /* 0                                  */
+  int64_t workspace_bytes;           /* fp32 workspace of a split, else 0  */
 } pgemm_kernel_info;
 
 pgemm_status pgemm_query(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K,
@@ -128,6 +148,14 @@ pgemm_status pgemm_query(pgemm_op op, int stages, int64_t M, int64_t N, int64_t 
  * up has still exited, but its output is undefined.
  */
 pgemm_status pgemm_sync_status(void *stream);
+
+/* Tuning and test hook: forces the tiling of later NT calls in this
+ * process.  tile: 0 = planned automatically, 128 or 256 = that output tile;
+ * k_split: 0 = planned automatically, 1 = no split, 2..16 = that many K
+ * pieces (small tiles only; fewer if K has fewer 64-wide pieces).
+ * PGEMM_ERR_SHAPE for any other combination (nothing changes).  Not meant
+ * to be changed while other threads launch. */
+pgemm_status pgemm_set_tiling(int tile, int k_split);
 
 /* Test hook for the credit protocol.  Sets, for later *_ws launches in this
  * process, the poll limit of every credit wait (0 restores the default) and

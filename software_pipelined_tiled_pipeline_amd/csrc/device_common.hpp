@@ -79,16 +79,22 @@ struct RingRow {
   __device__ __forceinline__ static int swz(int r) { return (r / ROWS_PER_WINDOW) % CPR; }
 };
 
-// Output tile for a workgroup.  Workgroups are dispatched round-robin over
-// the 8 XCDs, each with its own L2: ids are first regrouped so that every XCD
-// receives a contiguous run, then runs are walked in groups of `group_m`
-// row panels so that concurrently resident tiles share A and B panels.
-__device__ __forceinline__ void tile_of_block(int64_t bid, int64_t nblocks, int tiles_m, int tiles_n,
-                                              int group_m, int *bm, int *bn) {
+// Work of a workgroup: output tile (bm, bn) and K piece `split`.
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2: ids are first regrouped so that every XCD receives a contiguous run.
+// The K piece is the slowest-varying part of the id, so the workgroups of
+// one XCD share a K piece (and with it the slice of lhs they read); tiles
+// are then walked in groups of `group_m` row panels so that concurrently
+// resident tiles share A and B panels.
+__device__ __forceinline__ void block_work(int64_t bid, int64_t nblocks, int tiles_m, int tiles_n, int group_m,
+                                           int *bm, int *bn, int *split) {
   constexpr int kXcds = 8;
   int64_t per = nblocks / kXcds;
   int64_t id = bid;
   if (bid < per * kXcds) id = (bid % kXcds) * per + bid / kXcds;
+  const int64_t tiles = (int64_t)tiles_m * tiles_n;
+  *split = (int)(id / tiles);
+  id %= tiles;
   int64_t span = (int64_t)group_m * tiles_n;
   int64_t g = id / span;
   int64_t first = g * group_m;

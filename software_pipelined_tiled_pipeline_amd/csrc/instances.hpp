@@ -1,23 +1,34 @@
-// Kernel instances the library dispatches to, by variant and stage count.
+// Kernel instances the library dispatches to, by variant, tile size and
+// stage count.
 #pragma once
 
 #include "kernels.hpp"
 
 namespace pgemm {
 
-// Single schedule: 256 x 256 output tile, four waves (one per SIMD, up to
-// 512 registers each) of 128 x 128.  K tile 64 (64 KiB slots) for one or
-// two slots, 32 (32 KiB slots) for three or four.
+// Single schedule, large tile: 256 x 256 output tile, four waves (one per
+// SIMD, up to 512 registers each) of 128 x 128.  K tile 64 (64 KiB slots)
+// for one or two slots, 32 (32 KiB slots) for three or four.
 template <int S>
 using SwapGeom = NtGeom<256, 256, (S <= 2 ? 64 : 32), S, 2, 2, 0>;
 
-// Producer/consumer: 256 x 256 output tile, eight consumer waves of
-// 128 x 64 (two per SIMD) and four producer waves (one per SIMD), so every
-// wave is capped at 168 registers.  K tile 64 (64 KiB slots) for one or two
-// slots, 32 (32 KiB slots) for three or four, so that the ring and the
-// output staging tile fit in 160 KiB of LDS.
+// Producer/consumer, large tile: 256 x 256 output tile, eight consumer waves
+// of 128 x 64 (two per SIMD) and four producer waves (one per SIMD), so
+// every wave is capped at 168 registers.  K tile 64 (64 KiB slots) for one
+// or two slots, 32 (32 KiB slots) for three or four, so that the ring and
+// the output staging tile fit in 160 KiB of LDS.
 template <int S>
 using WsGeom = NtGeom<256, 256, (S <= 2 ? 64 : 32), S, 2, 4, 4>;
+
+// Small tile, for products with too few 256 x 256 tiles to fill the chip
+// (and, with a K split, for skinny ones): 128 x 128 output tile, K tile 64
+// (32 KiB slots, so four slots take 128 KiB).  Single schedule: four waves
+// of 64 x 64, two workgroups per CU where LDS allows.  Producer/consumer:
+// four consumer waves of 64 x 64 and two producer waves.
+template <int S>
+using SwapGeomSmall = NtGeom<128, 128, 64, S, 2, 2, 0, 2>;
+template <int S>
+using WsGeomSmall = NtGeom<128, 128, 64, S, 2, 2, 2>;
 
 constexpr int kSwapMaxStages = 4;
 constexpr int kSwapDefaultStages = 2;

@@ -110,17 +110,23 @@ struct SlotLoader {
   static_assert((BM * CPR) % kWave == 0 && (BN * CPR) % kWave == 0, "tiles fill whole instructions");
 
   __amdgpu_buffer_rsrc_t ra, rb;
-  int K;
+  int pitch;  // elements per row of lhs and rhs (the full K)
+  int klen;   // K extent this workgroup reads, from column kb on
   uint32_t lane_off[PAR];  // (l / CPR) * row bytes + chunk * 16, per parity
   int lane_k[PAR];         // chunk * 8: the lane's first k within the tile
 
-  __device__ __forceinline__ void init(const uint16_t *lhs, const uint16_t *rhs, int M, int N, int K_,
-                                       int m0, int n0) {
-    K = K_;
+  // Tiles cover rows m0.. of lhs and n0.. of rhs, columns kb .. kb+klen-1.
+  // The resources start at column kb and end at the last row's end, so a
+  // row past the matrix edge is out of range while every in-matrix element
+  // of the K range is inside.
+  __device__ __forceinline__ void init(const uint16_t *lhs, const uint16_t *rhs, int M, int N, int K, int kb,
+                                       int klen_, int m0, int n0) {
+    pitch = K;
+    klen = klen_;
     const int rows_a = M - m0 < BM ? M - m0 : BM;
     const int rows_b = N - n0 < BN ? N - n0 : BN;
-    ra = make_rsrc(lhs + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K * 2u);
-    rb = make_rsrc(rhs + (int64_t)n0 * K, (uint32_t)rows_b * (uint32_t)K * 2u);
+    ra = make_rsrc(lhs + (int64_t)m0 * K + kb, ((uint32_t)rows_a * (uint32_t)K - (uint32_t)kb) * 2u);
+    rb = make_rsrc(rhs + (int64_t)n0 * K + kb, ((uint32_t)rows_b * (uint32_t)K - (uint32_t)kb) * 2u);
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int p = 0; p < PAR; ++p) {
@@ -138,8 +144,8 @@ struct SlotLoader {
     const bool is_a = j < A_INSTR;
     const int jj = is_a ? j : j - A_INSTR;
     const int k0 = t * BK;
-    uint32_t voff = lane_off[p] + (uint32_t)(jj * RPI) * (uint32_t)K * 2u;
-    if (lane_k[p] >= K - k0) voff = kOobOffset;  // chunk past K (every lane, past the last tile)
+    uint32_t voff = lane_off[p] + (uint32_t)(jj * RPI) * (uint32_t)pitch * 2u;
+    if (lane_k[p] >= klen - k0) voff = kOobOffset;  // chunk past K (every lane, past the last tile)
     load_lds_x4(is_a ? ra : rb, slot + j * (kWave * 16), voff, (uint32_t)k0 * 2u);
   }
 
@@ -157,7 +163,7 @@ struct SlotLoader {
   template <int COUNT>
   __device__ __forceinline__ void fetch(u32x4 (&r)[COUNT], int t, int first, int lane) const {
     const int k0 = t * BK;
-    const bool whole = k0 + BK <= K;
+    const bool whole = k0 + BK <= klen;
 #pragma unroll
     for (int i = 0; i < COUNT; ++i) {
       const int j = first + i;
@@ -166,8 +172,8 @@ struct SlotLoader {
       const int row = jj * (kWave / CPR) + lane / CPR;
       const int chunk = (lane % CPR) ^ Row::swz(row);
       const int kc = k0 + chunk * 8;
-      uint32_t off = ((uint32_t)row * (uint32_t)K + (uint32_t)kc) * 2u;
-      if (!whole && kc >= K) off = kOobOffset;
+      uint32_t off = ((uint32_t)row * (uint32_t)pitch + (uint32_t)kc) * 2u;
+      if (!whole && kc >= klen) off = kOobOffset;
       r[i] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? ra : rb, (int)off, 0, 0);
     }
   }
@@ -207,10 +213,17 @@ struct Staging {
 // Geometry of one NT kernel instance: output tile BM x BN, K tile BK, S ring
 // slots, WGM x WGN math waves (each owning a (BM/WGM) x (BN/WGN) block) and
 // P producer waves (0 for the single-schedule kernel).
-template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_, int P_>
+//
+// Every NT kernel computes the K range [kb, kb + klen) of its tile, with
+// kb = split * k_chunk.  Without a K split (SPLIT false, one piece) that is
+// all of K and the epilogue rounds to T and stores the tile; with one, the
+// epilogue stores the fp32 tile into its piece's plane of `partial`
+// ([splits][M][ldp]) and reduce_splits adds the planes up afterwards.
+template <int BM_, int BN_, int BK_, int S_, int WGM_, int WGN_, int P_, int OCC_ = 1>
 struct NtGeom {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
   static constexpr int WGM = WGM_, WGN = WGN_, P = P_;
+  static constexpr int OCC = OCC_;  // waves per SIMD the register budget allows
   static constexpr int CW = WGM * WGN;  // math waves
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int THREADS = (CW + P) * kWave;
@@ -233,7 +246,7 @@ struct NtGeom {
   static_assert(Loader::INSTR % LOADERS == 0, "loads split evenly");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave blocks are whole 32x32 MFMA tiles");
   static_assert(S <= 4, "vmcnt wait table covers three tiles in flight");
-  static_assert(S * PER_LOADER < 64, "in-flight loads fit the 6-bit vmcnt");
+  static_assert(P > 0 || S * PER_LOADER < 64, "in-flight loads fit the 6-bit vmcnt");
 };
 
 // ======================================================= NT, single schedule
@@ -255,10 +268,11 @@ struct NtGeom {
 // The loads of a tile are issued S-1 tiles ahead (at the barrier in tile
 // t-S, when its slot comes free).  S = 1
 // has a single slot and runs fill -> barrier -> compute -> barrier.
-template <typename T, class G>
-__global__ void __launch_bounds__(G::THREADS, 1)
+template <typename T, class G, bool SPLIT>
+__global__ void __launch_bounds__(G::THREADS, G::OCC)
     nt_swap_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
-                   uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m) {
+                   uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m,
+                   int k_chunk, float *__restrict__ partial, int ldp) {
   static_assert(G::P == 0, "single-schedule kernel has no producer waves");
   using Loader = typename G::Loader;
   using Row = RingRow<G::BK>;
@@ -270,16 +284,18 @@ __global__ void __launch_bounds__(G::THREADS, 1)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int bm, bn;
-  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &bm, &bn);
+  int bm, bn, split;
+  block_work(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &bm, &bn, &split);
   const int m0 = bm * G::BM, n0 = bn * G::BN;
   const int wm = wave / G::WGN, wn = wave % G::WGN;
+  const int kb = split * k_chunk;
+  const int klen = K - kb < k_chunk ? K - kb : k_chunk;
 
   Loader ld;
-  ld.init(lhs, rhs, M, N, K, m0, n0);
+  ld.init(lhs, rhs, M, N, K, kb, klen, m0, n0);
   W w;
   w.zero();
-  const int n_k = (K + G::BK - 1) / G::BK;
+  const int n_k = klen > 0 ? (klen + G::BK - 1) / G::BK : 0;
   auto slot_ptr = [&](int s) { return smem + s * Loader::SLOT_BYTES; };
   const int first = wave * G::PER_LOADER;
   const int r = lane & 31, hi = lane >> 5, sw = Row::swz(r);
@@ -346,19 +362,24 @@ __global__ void __launch_bounds__(G::THREADS, 1)
       w.template mixed_step<false, 0>(f[1], f[0], lane_a(0), lane_b(0), 0, hi, sw, no_load);
     }
   }
-  __syncthreads();  // ring no longer read: reuse it as the staging tile
-  w.stage(smem, Staging<G::BN>::PITCH, wm * G::WM, wn * G::WN, lane);
-  __syncthreads();
-  store_staged<G::BM, G::BN, G::THREADS>(smem, Staging<G::BN>::PITCH, out, M, N, m0, n0, tid);
+  if constexpr (SPLIT) {
+    w.store_partial(partial + (int64_t)split * M * ldp, ldp, M, N, m0 + wm * G::WM, n0 + wn * G::WN, lane);
+  } else {
+    __syncthreads();  // ring no longer read: reuse it as the staging tile
+    w.stage(smem, Staging<G::BN>::PITCH, wm * G::WM, wn * G::WN, lane);
+    __syncthreads();
+    store_staged<G::BM, G::BN, G::THREADS>(smem, Staging<G::BN>::PITCH, out, M, N, m0, n0, tid);
+  }
 }
 
 // ========================================================= NT, WS (credits)
 
-template <typename T, class G>
+template <typename T, class G, bool SPLIT>
 __global__ void __launch_bounds__(G::THREADS)
     nt_ws_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
                  uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m,
-                 uint32_t max_polls, int skip_seed, uint32_t *err) {
+                 int k_chunk, float *__restrict__ partial, int ldp, uint32_t max_polls, int skip_seed,
+                 uint32_t *err) {
   static_assert(G::P > 0, "producer/consumer kernel needs producer waves");
   using Loader = typename G::Loader;
   using Row = RingRow<G::BK>;
@@ -369,10 +390,12 @@ __global__ void __launch_bounds__(G::THREADS)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int bm, bn;
-  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &bm, &bn);
+  int bm, bn, split;
+  block_work(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, &bm, &bn, &split);
   const int m0 = bm * G::BM, n0 = bn * G::BN;
-  const int n_k = (K + G::BK - 1) / G::BK;
+  const int kb = split * k_chunk;
+  const int klen = K - kb < k_chunk ? K - kb : k_chunk;
+  const int n_k = klen > 0 ? (klen + G::BK - 1) / G::BK : 0;
   auto slot_ptr = [&](int s) { return smem + s * Loader::SLOT_BYTES; };
 
   if (tid < 2 * S) full[tid] = 0u;  // full[0..S) and empty[0..S)
@@ -398,7 +421,7 @@ __global__ void __launch_bounds__(G::THREADS)
   } else {
     // ---------------------------------------------------------- producer
     Loader ld;
-    ld.init(lhs, rhs, M, N, K, m0, n0);
+    ld.init(lhs, rhs, M, N, K, kb, klen, m0, n0);
     const int first = (wave - C) * G::PER_LOADER;
     constexpr int R = G::RBUF;
     u32x4 buf[R][G::PER_LOADER];
@@ -420,10 +443,15 @@ __global__ void __launch_bounds__(G::THREADS)
       }
     }
   }
-  __syncthreads();  // all tiles consumed: the ring becomes the staging tile
-  if (wave < C) w.stage(smem, Staging<G::BN>::PITCH, wm * G::WM, wn * G::WN, lane);
-  __syncthreads();
-  store_staged<G::BM, G::BN, G::THREADS>(smem, Staging<G::BN>::PITCH, out, M, N, m0, n0, tid);
+  if constexpr (SPLIT) {
+    if (wave < C)
+      w.store_partial(partial + (int64_t)split * M * ldp, ldp, M, N, m0 + wm * G::WM, n0 + wn * G::WN, lane);
+  } else {
+    __syncthreads();  // all tiles consumed: the ring becomes the staging tile
+    if (wave < C) w.stage(smem, Staging<G::BN>::PITCH, wm * G::WM, wn * G::WN, lane);
+    __syncthreads();
+    store_staged<G::BM, G::BN, G::THREADS>(smem, Staging<G::BN>::PITCH, out, M, N, m0, n0, tid);
+  }
 }
 
 }  // namespace pgemm

@@ -1,14 +1,15 @@
-// C-ABI of the pgemm library: argument checks, kernel choice, launch.
+// C-ABI of the pgemm library: argument checks, planning, launch.
 //
-// Every call validates its arguments before touching HIP, picks one kernel
-// instance from (element type, variant, stages), and enqueues it on the
-// caller's stream without waiting.
+// Every call validates its arguments before touching HIP, plans the launch
+// (tile size, ring slots, K split) on the host, and enqueues its kernels on
+// the caller's stream without waiting.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "pgemm.h"
 #include "instances.hpp"
@@ -31,12 +32,38 @@ constexpr uint32_t kDefaultPolls = 1u << 24;
 std::atomic<uint32_t> g_max_polls{kDefaultPolls};
 std::atomic<int> g_skip_seed{0};
 
-// ------------------------------------------------------------- geometry
+// ------------------------------------------------------------- planning
+//
+// The plan of an NT call: tile size, ring slots and K split.  Large
+// (256 x 256) tiles when they alone nearly fill the chip, small (128 x 128)
+// ones otherwise; a product that even then leaves most CUs idle and has a
+// long K is split along K into pieces whose fp32 partial tiles a second
+// kernel adds up.  pgemm_set_tiling can force either choice.
+
+constexpr int kLargeTile = 256, kSmallTile = 128;
+constexpr int64_t kFillTiles = 192;   // 3/4 of the 256 CUs
+constexpr int64_t kSplitBelow = 128;  // small tiles that leave half the CUs idle
+constexpr int kMaxSplit = 16;
+constexpr int64_t kMinPieceK = 512;   // K elements per piece, at least
+constexpr int kPieceAlign = 64;       // the small tile's K tile
+
+std::atomic<int> g_force_tile{0};
+std::atomic<int> g_force_split{0};
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+struct Plan {
+  int tile = 0;         // 256 or 128 (NT calls), 16 (int32 call)
+  int stages = 0;
+  int split = 1;        // K pieces
+  int64_t k_chunk = 0;  // K elements per piece (K itself without a split)
+  int64_t ldp = 0;      // row pitch of the partial-sum planes, in floats
+  pgemm_kernel_info info{};
+};
+
 template <class G>
-void fill_nt(pgemm_kernel_info *i, int64_t M, int64_t N, int64_t K) {
+void fill_nt(Plan *p, int64_t M, int64_t N) {
+  pgemm_kernel_info *i = &p->info;
   i->block_m = G::BM;
   i->block_n = G::BN;
   i->block_k = G::BK;
@@ -45,18 +72,64 @@ void fill_nt(pgemm_kernel_info *i, int64_t M, int64_t N, int64_t K) {
   i->consumer_waves = G::CW;
   i->threads = G::THREADS;
   i->lds_bytes = G::LDS_BYTES;
-  i->grid = cdiv(M, G::BM) * cdiv(N, G::BN);
-  i->k_tiles = cdiv(K, G::BK);
+  i->grid = cdiv(M, G::BM) * cdiv(N, G::BN) * p->split;
+  i->k_tiles = cdiv(p->k_chunk, G::BK);
+  i->k_split = p->split;
+  i->workspace_bytes = p->split > 1 ? p->split * M * p->ldp * (int64_t)sizeof(float) : 0;
 }
 
-pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, pgemm_kernel_info *info,
-                  int *stages_out) {
+template <template <int> class Geo>
+bool fill_nt_s(Plan *p, int s, int64_t M, int64_t N) {
+  switch (s) {
+    case 1: fill_nt<Geo<1>>(p, M, N); return true;
+    case 2: fill_nt<Geo<2>>(p, M, N); return true;
+    case 3: fill_nt<Geo<3>>(p, M, N); return true;
+    case 4: fill_nt<Geo<4>>(p, M, N); return true;
+  }
+  return false;
+}
+
+void choose_tiling(Plan *p, int64_t M, int64_t N, int64_t K) {
+  const int force_tile = g_force_tile.load(std::memory_order_relaxed);
+  const int force_split = g_force_split.load(std::memory_order_relaxed);
+  const int64_t large = cdiv(M, kLargeTile) * cdiv(N, kLargeTile);
+  p->tile = force_tile ? force_tile : (large >= kFillTiles ? kLargeTile : kSmallTile);
+  int split = 1;
+  if (p->tile == kSmallTile && K > 0) {
+    const int64_t small = cdiv(M, kSmallTile) * cdiv(N, kSmallTile);
+    if (force_split) {
+      split = force_split;
+    } else if (small < kSplitBelow && K >= 2 * kMinPieceK) {
+      int64_t want = 2 * kSplitBelow / (small > 0 ? small : 1);
+      if (want > kMaxSplit) want = kMaxSplit;
+      if (want > K / kMinPieceK) want = K / kMinPieceK;
+      split = (int)(want < 1 ? 1 : want);
+    }
+  }
+  p->split = 1;
+  p->k_chunk = K;
+  if (split > 1) {
+    p->k_chunk = cdiv(cdiv(K, split), kPieceAlign) * kPieceAlign;
+    p->split = (int)cdiv(K, p->k_chunk);  // no empty pieces
+    if (p->split <= 1) {
+      p->split = 1;
+      p->k_chunk = K;
+    }
+  }
+  p->ldp = cdiv(N, 4) * 4;
+}
+
+pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, Plan *p) {
   if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return PGEMM_ERR_SHAPE;
-  std::memset(info, 0, sizeof *info);
+  *p = Plan{};
+  pgemm_kernel_info *info = &p->info;
   switch (op) {
     case PGEMM_OP_S32_NN: {
-      int s = stages == 0 ? 2 : stages;
+      const int s = stages == 0 ? 2 : stages;
       if (s != 1 && s != 2) return PGEMM_ERR_STAGES;
+      p->tile = 16;
+      p->stages = s;
+      p->k_chunk = K;
       info->block_m = 16;
       info->block_n = 16;
       info->block_k = 16;
@@ -66,29 +139,23 @@ pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, pgem
       info->lds_bytes = s * 2 * 16 * 16 * 4;
       info->grid = cdiv(M, 16) * cdiv(N, 16);
       info->k_tiles = cdiv(K, 16);
-      *stages_out = s;
+      info->k_split = 1;
       return PGEMM_OK;
     }
-    case PGEMM_OP_NT_SWAP: {
-      if (K >= kMaxKNt) return PGEMM_ERR_SHAPE;
-      int s = stages == 0 ? kSwapDefaultStages : stages;
-      if (s == 1) fill_nt<SwapGeom<1>>(info, M, N, K);
-      else if (s == 2) fill_nt<SwapGeom<2>>(info, M, N, K);
-      else if (s == 3) fill_nt<SwapGeom<3>>(info, M, N, K);
-      else if (s == 4) fill_nt<SwapGeom<4>>(info, M, N, K);
-      else return PGEMM_ERR_STAGES;
-      *stages_out = s;
-      break;
-    }
+    case PGEMM_OP_NT_SWAP:
     case PGEMM_OP_NT_WS: {
       if (K >= kMaxKNt) return PGEMM_ERR_SHAPE;
-      int s = stages == 0 ? kWsDefaultStages : stages;
-      if (s == 1) fill_nt<WsGeom<1>>(info, M, N, K);
-      else if (s == 2) fill_nt<WsGeom<2>>(info, M, N, K);
-      else if (s == 3) fill_nt<WsGeom<3>>(info, M, N, K);
-      else if (s == 4) fill_nt<WsGeom<4>>(info, M, N, K);
-      else return PGEMM_ERR_STAGES;
-      *stages_out = s;
+      const bool ws = op == PGEMM_OP_NT_WS;
+      const int s = stages == 0 ? (ws ? kWsDefaultStages : kSwapDefaultStages) : stages;
+      if (s < 1 || s > (ws ? kWsMaxStages : kSwapMaxStages)) return PGEMM_ERR_STAGES;
+      p->stages = s;
+      choose_tiling(p, M, N, K);
+      bool ok;
+      if (p->tile == kLargeTile)
+        ok = ws ? fill_nt_s<WsGeom>(p, s, M, N) : fill_nt_s<SwapGeom>(p, s, M, N);
+      else
+        ok = ws ? fill_nt_s<WsGeomSmall>(p, s, M, N) : fill_nt_s<SwapGeomSmall>(p, s, M, N);
+      if (!ok) return PGEMM_ERR_STAGES;
       break;
     }
     default:
@@ -155,32 +222,98 @@ pgemm_status check_ptrs(const void *lhs, const void *rhs, const void *out, int64
 
 pgemm_status launched() { return hipGetLastError() == hipSuccess ? PGEMM_OK : PGEMM_ERR_LAUNCH; }
 
-template <typename T, class G>
-pgemm_status launch_swap(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int M, int N, int K,
-                         hipStream_t stream, int dev) {
-  auto kern = nt_swap_kernel<T, G>;
+// ------------------------------------------------------------ workspace
+//
+// fp32 partial sums of K-split products: one buffer per (device, stream),
+// grown on demand and kept until the process ends, so that launches on
+// different streams never share one and launches on one stream are ordered.
+struct Workspace {
+  int dev;
+  void *stream;
+  float *ptr;
+  size_t bytes;
+};
+std::mutex g_work_mutex;
+std::vector<Workspace> g_work;
+
+pgemm_status workspace(int dev, hipStream_t stream, size_t bytes, float **out) {
+  std::lock_guard<std::mutex> lock(g_work_mutex);
+  Workspace *w = nullptr;
+  for (auto &e : g_work)
+    if (e.dev == dev && e.stream == static_cast<void *>(stream)) w = &e;
+  if (!w) {
+    g_work.push_back(Workspace{dev, static_cast<void *>(stream), nullptr, 0});
+    w = &g_work.back();
+  }
+  if (w->bytes < bytes) {
+    if (w->ptr) {
+      // earlier launches on this stream may still read the old buffer
+      if (hipStreamSynchronize(stream) != hipSuccess) return PGEMM_ERR_LAUNCH;
+      if (hipFree(w->ptr) != hipSuccess) return PGEMM_ERR_LAUNCH;
+      w->ptr = nullptr;
+      w->bytes = 0;
+    }
+    void *p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return PGEMM_ERR_NOMEM;
+    }
+    w->ptr = static_cast<float *>(p);
+    w->bytes = bytes;
+  }
+  *out = w->ptr;
+  return PGEMM_OK;
+}
+
+// --------------------------------------------------------------- launch
+
+struct NtArgs {
+  const uint16_t *lhs, *rhs;
+  uint16_t *out;
+  int M, N, K;
+  hipStream_t stream;
+  int dev;
+};
+
+template <typename T, class G, bool SPLIT, bool WS>
+pgemm_status launch_nt(const NtArgs &a, const Plan &p, float *part) {
   static std::atomic<uint64_t> lds_set{0};
-  pgemm_status st = allow_lds(kern, G::LDS_BYTES, dev, lds_set);
-  if (st != PGEMM_OK) return st;
-  const int tm = (int)cdiv(M, G::BM), tn = (int)cdiv(N, G::BN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tm * (int64_t)tn)), dim3(G::THREADS), G::LDS_BYTES, stream, lhs, rhs,
-                     out, M, N, K, tm, tn, kGroupM);
+  const int tm = (int)cdiv(a.M, G::BM), tn = (int)cdiv(a.N, G::BN);
+  const dim3 grid((unsigned)((int64_t)tm * tn * p.split));
+  const int k_chunk = (int)p.k_chunk, ldp = (int)p.ldp;
+  if constexpr (WS) {
+    auto kern = nt_ws_kernel<T, G, SPLIT>;
+    pgemm_status st = allow_lds(kern, G::LDS_BYTES, a.dev, lds_set);
+    if (st != PGEMM_OK) return st;
+    const uint32_t polls = g_max_polls.load(std::memory_order_relaxed);
+    const int skip = g_skip_seed.load(std::memory_order_relaxed);
+    hipLaunchKernelGGL(kern, grid, dim3(G::THREADS), G::LDS_BYTES, a.stream, a.lhs, a.rhs, a.out, a.M, a.N, a.K, tm,
+                       tn, kGroupM, k_chunk, part, ldp, polls, skip, g_err_ptr[a.dev]);
+  } else {
+    auto kern = nt_swap_kernel<T, G, SPLIT>;
+    pgemm_status st = allow_lds(kern, G::LDS_BYTES, a.dev, lds_set);
+    if (st != PGEMM_OK) return st;
+    hipLaunchKernelGGL(kern, grid, dim3(G::THREADS), G::LDS_BYTES, a.stream, a.lhs, a.rhs, a.out, a.M, a.N, a.K, tm,
+                       tn, kGroupM, k_chunk, part, ldp);
+  }
+  pgemm_status st = launched();
+  if (st != PGEMM_OK || !SPLIT) return st;
+  int64_t blocks = cdiv((int64_t)a.M * (p.ldp / 4), 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(reduce_splits<T>, dim3((unsigned)blocks), dim3(256), 0, a.stream, part, a.out, a.M, a.N, ldp,
+                     p.split);
   return launched();
 }
 
-template <typename T, class G>
-pgemm_status launch_ws(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int M, int N, int K,
-                       hipStream_t stream, int dev) {
-  auto kern = nt_ws_kernel<T, G>;
-  static std::atomic<uint64_t> lds_set{0};
-  pgemm_status st = allow_lds(kern, G::LDS_BYTES, dev, lds_set);
-  if (st != PGEMM_OK) return st;
-  const int tm = (int)cdiv(M, G::BM), tn = (int)cdiv(N, G::BN);
-  uint32_t polls = g_max_polls.load(std::memory_order_relaxed);
-  int skip = g_skip_seed.load(std::memory_order_relaxed);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tm * (int64_t)tn)), dim3(G::THREADS), G::LDS_BYTES, stream, lhs, rhs, out,
-                     M, N, K, tm, tn, kGroupM, polls, skip, g_err_ptr[dev]);
-  return launched();
+template <typename T, template <int> class Geo, bool SPLIT, bool WS>
+pgemm_status launch_nt_s(const NtArgs &a, const Plan &p, float *part) {
+  switch (p.stages) {
+    case 1: return launch_nt<T, Geo<1>, SPLIT, WS>(a, p, part);
+    case 2: return launch_nt<T, Geo<2>, SPLIT, WS>(a, p, part);
+    case 3: return launch_nt<T, Geo<3>, SPLIT, WS>(a, p, part);
+    case 4: return launch_nt<T, Geo<4>, SPLIT, WS>(a, p, part);
+  }
+  return PGEMM_ERR_STAGES;
 }
 
 template <typename T>
@@ -188,33 +321,26 @@ pgemm_status nt_entry(pgemm_op op, const uint16_t *lhs, const uint16_t *rhs, uin
                       int64_t K, int stages, void *stream) {
   pgemm_status st = check_ptrs(lhs, rhs, out, M, N, K);
   if (st != PGEMM_OK) return st;
-  pgemm_kernel_info info;
-  int s = 0;
-  st = plan(op, stages, M, N, K, &info, &s);
+  Plan p;
+  st = plan(op, stages, M, N, K, &p);
   if (st != PGEMM_OK) return st;
   if (K % 8 != 0) return PGEMM_ERR_ALIGN;  // rows of lhs/rhs must start on 16 bytes
   if (M == 0 || N == 0) return PGEMM_OK;
-  int dev = 0;
-  st = current_device(&dev);
+  NtArgs a{lhs, rhs, out, (int)M, (int)N, (int)K, static_cast<hipStream_t>(stream), 0};
+  st = current_device(&a.dev);
   if (st != PGEMM_OK) return st;
-  hipStream_t h = static_cast<hipStream_t>(stream);
-  const int m = (int)M, n = (int)N, k = (int)K;
-  if (op == PGEMM_OP_NT_SWAP) {
-    switch (s) {
-      case 1: return launch_swap<T, SwapGeom<1>>(lhs, rhs, out, m, n, k, h, dev);
-      case 2: return launch_swap<T, SwapGeom<2>>(lhs, rhs, out, m, n, k, h, dev);
-      case 3: return launch_swap<T, SwapGeom<3>>(lhs, rhs, out, m, n, k, h, dev);
-      case 4: return launch_swap<T, SwapGeom<4>>(lhs, rhs, out, m, n, k, h, dev);
-    }
-  } else {
-    switch (s) {
-      case 1: return launch_ws<T, WsGeom<1>>(lhs, rhs, out, m, n, k, h, dev);
-      case 2: return launch_ws<T, WsGeom<2>>(lhs, rhs, out, m, n, k, h, dev);
-      case 3: return launch_ws<T, WsGeom<3>>(lhs, rhs, out, m, n, k, h, dev);
-      case 4: return launch_ws<T, WsGeom<4>>(lhs, rhs, out, m, n, k, h, dev);
-    }
-  }
-  return PGEMM_ERR_STAGES;
+  const bool ws = op == PGEMM_OP_NT_WS;
+  if (p.tile == kLargeTile)
+    return ws ? launch_nt_s<T, WsGeom, false, true>(a, p, nullptr)
+              : launch_nt_s<T, SwapGeom, false, false>(a, p, nullptr);
+  if (p.split == 1)
+    return ws ? launch_nt_s<T, WsGeomSmall, false, true>(a, p, nullptr)
+              : launch_nt_s<T, SwapGeomSmall, false, false>(a, p, nullptr);
+  float *part = nullptr;
+  st = workspace(a.dev, a.stream, (size_t)p.info.workspace_bytes, &part);
+  if (st != PGEMM_OK) return st;
+  return ws ? launch_nt_s<T, WsGeomSmall, true, true>(a, p, part)
+            : launch_nt_s<T, SwapGeomSmall, true, false>(a, p, part);
 }
 
 }  // namespace
@@ -225,9 +351,8 @@ pgemm_status pgemm_s32_nn(const int32_t *lhs, const int32_t *rhs, int32_t *out, 
                           int stages, void *stream) {
   pgemm_status st = check_ptrs(lhs, rhs, out, M, N, K);
   if (st != PGEMM_OK) return st;
-  pgemm_kernel_info info;
-  int s = 0;
-  st = plan(PGEMM_OP_S32_NN, stages, M, N, K, &info, &s);
+  Plan p;
+  st = plan(PGEMM_OP_S32_NN, stages, M, N, K, &p);
   if (st != PGEMM_OK) return st;
   if (M == 0 || N == 0) return PGEMM_OK;
   int dev = 0;
@@ -235,7 +360,7 @@ pgemm_status pgemm_s32_nn(const int32_t *lhs, const int32_t *rhs, int32_t *out, 
   if (st != PGEMM_OK) return st;
   const dim3 grid((unsigned)cdiv(M, 16), (unsigned)cdiv(N, 16));
   hipStream_t h = static_cast<hipStream_t>(stream);
-  if (s == 1)
+  if (p.stages == 1)
     hipLaunchKernelGGL(s32_nn_kernel<1>, grid, dim3(256), 0, h, lhs, rhs, out, (int)M, (int)N, (int)K);
   else
     hipLaunchKernelGGL(s32_nn_kernel<2>, grid, dim3(256), 0, h, lhs, rhs, out, (int)M, (int)N, (int)K);
@@ -264,8 +389,19 @@ pgemm_status pgemm_bf16_nt_ws(const uint16_t *lhs, const uint16_t *rhs, uint16_t
 
 pgemm_status pgemm_query(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, pgemm_kernel_info *info) {
   if (!info) return PGEMM_ERR_NULL;
-  int s = 0;
-  return plan(op, stages, M, N, K, info, &s);
+  Plan p;
+  pgemm_status st = plan(op, stages, M, N, K, &p);
+  if (st == PGEMM_OK) *info = p.info;
+  return st;
+}
+
+pgemm_status pgemm_set_tiling(int tile, int k_split) {
+  if (tile != 0 && tile != kLargeTile && tile != kSmallTile) return PGEMM_ERR_SHAPE;
+  if (k_split < 0 || k_split > kMaxSplit) return PGEMM_ERR_SHAPE;
+  if (k_split > 1 && tile != kSmallTile) return PGEMM_ERR_SHAPE;
+  g_force_tile.store(tile, std::memory_order_relaxed);
+  g_force_split.store(k_split, std::memory_order_relaxed);
+  return PGEMM_OK;
 }
 
 pgemm_status pgemm_sync_status(void *stream) {
@@ -294,13 +430,14 @@ const char *pgemm_strerror(pgemm_status status) {
   switch (status) {
     case PGEMM_OK: return "ok";
     case PGEMM_ERR_NULL: return "a required pointer is NULL";
-    case PGEMM_ERR_SHAPE: return "M, N or K out of range";
+    case PGEMM_ERR_SHAPE: return "M, N or K out of range, or an unsupported tiling request";
     case PGEMM_ERR_STAGES: return "unsupported number of stages";
     case PGEMM_ERR_ALIGN: return "pointer not 16-byte aligned, or K not a multiple of 8 for an NT call";
     case PGEMM_ERR_LDS: return "tile ring exceeds the LDS budget";
     case PGEMM_ERR_LAUNCH: return "HIP launch or query failed";
     case PGEMM_ERR_TIMEOUT: return "a credit wait exceeded its poll limit";
     case PGEMM_ERR_DEVICE: return "current device is not gfx950";
+    case PGEMM_ERR_NOMEM: return "could not allocate the K-split workspace";
   }
   return "unknown status";
 }

@@ -139,7 +139,7 @@ struct WaveTile {
     static_assert(NM % NR == 0 || !READS, "reads spread evenly");
     static_assert(NLOAD == 0 || NM % NLOAD == 0, "loads spread evenly");
     constexpr int RE = NM / NR;                         // MFMAs per read
-    constexpr int LE = NLOAD > 0 ? NM / NLOAD : NM + 1;  // MFMAs per load
+    constexpr int LE = NLOAD > 0 ? NM / (NLOAD > 0 ? NLOAD : 1) : NM + 1;  // MFMAs per load
     const int p = ((2 * nkk + hi) ^ s) * 16;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -161,6 +161,30 @@ struct WaveTile {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+  }
+
+  // Writes the fp32 accumulators, unrounded, to a row-major partial-sum
+  // matrix (row pitch ldp floats, a multiple of 4) at (row0, col0); rows
+  // past M and column groups past N are skipped.  Each lane stores 16 bytes
+  // (four consecutive columns) per register quad.
+  __device__ __forceinline__ void store_partial(float *base, int ldp, int M, int N, int row0, int col0,
+                                                int lane) const {
+    const int r = lane & 31;
+    const int hi = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = row0 + 32 * i + r;
+      if (row >= M) continue;
+      float *rp = base + (int64_t)row * ldp;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = col0 + 32 * j + 8 * q + 4 * hi;
+          const f32x16 &a = acc[i][j];
+          if (col < N) *reinterpret_cast<f32x4 *>(rp + col) = f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+        }
+    }
   }
 
   // Rounds the accumulators to T and writes them into an LDS staging tile
@@ -204,6 +228,34 @@ __device__ __forceinline__ void store_staged(const char *st, int pitch, uint16_t
 #pragma unroll
       for (int x = 0; x < 8; ++x)
         if (gn + x < N) dst[x] = (uint16_t)(v[x / 2] >> (16 * (x % 2)));
+    }
+  }
+}
+
+// out[m][n] = round_T(sum over s of part[s][m][n]) for the K pieces of a
+// split product, summed in increasing s (so the result does not depend on
+// the order in which the pieces finished).  part is [splits][M][ldp] fp32.
+template <typename T>
+__global__ void __launch_bounds__(256) reduce_splits(const float *__restrict__ part, uint16_t *__restrict__ out,
+                                                     int M, int N, int ldp, int splits) {
+  const int64_t q = ldp / 4;
+  const int64_t total = (int64_t)M * q;
+  const int64_t plane = (int64_t)M * ldp;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int row = (int)(idx / q);
+    const int col = (int)(idx % q) * 4;
+    if (col >= N) continue;
+    const float *p = part + (int64_t)row * ldp + col;
+    f32x4 s = *reinterpret_cast<const f32x4 *>(p);
+    for (int k = 1; k < splits; ++k) s = s + *reinterpret_cast<const f32x4 *>(p + k * plane);
+    const u32x2 v = Mfma<T>::pack4(s[0], s[1], s[2], s[3]);
+    uint16_t *dst = out + (int64_t)row * N + col;
+    if ((N & 3) == 0) {
+      *reinterpret_cast<u32x2 *>(dst) = v;
+    } else {
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        if (col + x < N) dst[x] = (uint16_t)(v[x / 2] >> (16 * (x % 2)));
     }
   }
 }

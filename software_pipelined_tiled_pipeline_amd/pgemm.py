@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libpgemm.so")
 STATUS = {
     0: "PGEMM_OK", 1: "PGEMM_ERR_NULL", 2: "PGEMM_ERR_SHAPE", 3: "PGEMM_ERR_STAGES",
     4: "PGEMM_ERR_ALIGN", 5: "PGEMM_ERR_LDS", 6: "PGEMM_ERR_LAUNCH", 7: "PGEMM_ERR_TIMEOUT",
-    8: "PGEMM_ERR_DEVICE",
+    8: "PGEMM_ERR_DEVICE", 9: "PGEMM_ERR_NOMEM",
 }
 OPS = {"s32_nn": 0, "nt_swap": 1, "nt_ws": 2}
 GEMM_SYMBOLS = ("pgemm_s32_nn", "pgemm_f16_nt", "pgemm_f16_nt_ws", "pgemm_bf16_nt", "pgemm_bf16_nt_ws")
@@ -32,7 +32,8 @@ class PgemmError(RuntimeError):
 class KernelInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "block_m", "block_n", "block_k", "stages", "producer_waves", "consumer_waves", "threads", "lds_bytes")] + [
-        ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64)]
+        ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("k_split", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
 
 
 _lib = None
@@ -54,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.pgemm_query.restype = I
         L.pgemm_sync_status.argtypes = [P]
         L.pgemm_sync_status.restype = I
+        L.pgemm_set_tiling.argtypes = [I, I]
+        L.pgemm_set_tiling.restype = I
         L.pgemm_set_ws_debug.argtypes = [I64, I]
         L.pgemm_set_ws_debug.restype = None
         L.pgemm_strerror.argtypes = [I]
@@ -140,6 +143,11 @@ def pgemm_query(op: str, stages: int, M: int, N: int, K: int) -> dict:
 
 def pgemm_sync_status(stream=None) -> int:
     return lib().pgemm_sync_status(_stream(stream))
+
+
+def pgemm_set_tiling(tile: int = 0, k_split: int = 0) -> None:
+    """Forces the tiling of later NT calls (0, 0 restores the planner)."""
+    _check(lib().pgemm_set_tiling(int(tile), int(k_split)), "pgemm_set_tiling")
 
 
 def pgemm_set_ws_debug(max_polls: int = 0, skip_seed: bool = False) -> None:

@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_messages(L):
-    assert pgemm.abi_version() == 1
-    for code in range(9):
+    assert pgemm.abi_version() == 2
+    for code in range(10):
         assert pgemm.strerror(code) and pgemm.strerror(code) != "unknown status"
     assert pgemm.strerror(99) == "unknown status"
 
@@ -59,6 +59,60 @@ def test_query_geometry(L):
         ring = s * (q["block_m"] + q["block_n"]) * q["block_k"] * 2
         assert ring <= q["lds_bytes"]
     assert pgemm.pgemm_query("nt_ws", 0, 64, 64, 64)["stages"] == 4
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("op", ["nt_swap", "nt_ws"])
+def test_planner_on_the_workloads(L, op):
+    # 8192^3 and 4096^3: 1024 and 256 large tiles, enough to fill the chip
+    for n in (8192, 4096):
+        q = pgemm.pgemm_query(op, 0, n, n, n)
+        assert (q["block_m"], q["block_n"], q["k_split"]) == (256, 256, 1)
+        assert q["grid"] == (n // 256) ** 2 and q["workspace_bytes"] == 0
+    # ragged bf16 4095 x 1000 x 1000: 64 large tiles, so small ones (256)
+    q = pgemm.pgemm_query(op, 0, 4095, 1000, 1000)
+    assert (q["block_m"], q["block_n"], q["k_split"], q["grid"]) == (128, 128, 1, 32 * 8)
+    # skinny 128 x 8192 x 16384: 64 small tiles, K split in 4 pieces of 4096
+    q = pgemm.pgemm_query(op, 0, 128, 8192, 16384)
+    assert (q["block_m"], q["block_n"], q["k_split"], q["grid"]) == (128, 128, 4, 256)
+    assert q["k_tiles"] == 4096 // 64
+    assert q["workspace_bytes"] == 4 * 128 * 8192 * 4
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (128, 128, 1024), (100, 300, 1000), (64, 64, 4096), (7, 9000, 2 ** 21),
+                                   (2000, 2000, 64), (256, 768, 40000)])
+@pytest.mark.parametrize("force", [(0, 0), (128, 0), (128, 1), (128, 2), (128, 3), (128, 16), (256, 0)])
+def test_planner_invariants(L, M, N, K, force):
+    pgemm.pgemm_set_tiling(*force)
+    try:
+        for op in ("nt_swap", "nt_ws"):
+            q = pgemm.pgemm_query(op, 0, M, N, K)
+            if force[0]:
+                assert q["block_m"] == q["block_n"] == force[0]
+            split = q["k_split"]
+            assert split >= 1 and q["grid"] == cdiv(M, q["block_m"]) * cdiv(N, q["block_n"]) * split
+            if split == 1:
+                assert q["k_tiles"] == cdiv(K, q["block_k"]) and q["workspace_bytes"] == 0
+            else:
+                assert q["block_m"] == 128 and (force[1] == 0 or split <= force[1])
+                chunk = q["k_tiles"] * q["block_k"]
+                assert chunk % 64 == 0
+                assert (split - 1) * chunk < K <= split * chunk  # no empty piece
+                assert q["workspace_bytes"] == split * M * (cdiv(N, 4) * 4) * 4
+            if force[1] == 1:
+                assert split == 1
+            assert q["lds_bytes"] <= 160 * 1024
+    finally:
+        pgemm.pgemm_set_tiling(0, 0)
+
+
+def test_set_tiling_rejects(L):
+    for tile, split in [(100, 0), (64, 0), (256, 2), (0, 2), (0, 17), (128, -1), (128, 17)]:
+        assert L.pgemm_set_tiling(tile, split) == ERR_SHAPE
+    assert pgemm.pgemm_query("nt_ws", 0, 8192, 8192, 8192)["block_m"] == 256  # nothing changed
 
 
 @pytest.mark.parametrize("op,stages", [("s32_nn", 3), ("nt_swap", 5), ("nt_ws", 5), ("nt_ws", -1)])

@@ -5,9 +5,12 @@ element, |gpu - ref| <= 1e-3 * sum_k |a*b| + ulp(RNE(ref)) in the output
 type, with ref and sum_k |a*b| from the binary64 oracle.  Small shapes are
 compared in full; the full-size workloads are compared on sampled elements
 (the oracle computes each one alone) plus whole edge rows and columns, and
-across stages and variants for bit identity (every kernel accumulates the
-k16 MFMA steps in the same order).
+across stages, variants and tile sizes for bit identity (every kernel
+accumulates the k16 MFMA steps of an element in the same order; only a K
+split changes the order, into per-piece sums added in piece order).
 """
+import contextlib
+
 import numpy as np
 import pytest
 
@@ -52,6 +55,17 @@ def assert_within_bound(fmt, got, ref, mag, what):
 
 
 VARIANTS = [("swap", 1), ("swap", 2), ("swap", 3), ("swap", 4), ("ws", 1), ("ws", 2), ("ws", 3), ("ws", 4)]
+# (tile, k_split) forced through pgemm_set_tiling; (0, 0) is the planner's choice
+TILINGS = [(256, 0), (128, 1), (128, 3)]
+
+
+@contextlib.contextmanager
+def tiling(pg, tile, split):
+    pg.pgemm_set_tiling(tile, split)
+    try:
+        yield
+    finally:
+        pg.pgemm_set_tiling(0, 0)
 
 
 # ------------------------------------------------------------------ int32
@@ -88,20 +102,34 @@ def test_nt_small_all_variants(pg, fmt, M, N, K):
     A, B = inputs.make_operands(kind, M, N, K, 1000 + M + N + K)
     ref, mag = oracle.gemm_nt(fmt, A, B)
     dA, dB = dev_half(A, fmt), dev_half(B, fmt)
-    first = None
-    for variant, s in VARIANTS:
-        got = run_nt(pg, fmt, variant, A, B, s, dA, dB)
-        assert_within_bound(fmt, got, ref, mag, f"{fmt} {variant} S={s} {M}x{N}x{K}")
-        if first is None:
-            first = got
-        else:
-            assert np.array_equal(got, first), f"{variant} S={s} differs in bits from swap S=1"
+    unsplit = None
+    for tile, split in TILINGS:
+        with tiling(pg, tile, split):
+            pieces = pg.pgemm_query("nt_ws", 0, M, N, K)["k_split"]
+            first = None
+            for variant, s in VARIANTS:
+                got = run_nt(pg, fmt, variant, A, B, s, dA, dB)
+                what = f"{fmt} {variant} S={s} tile {tile} pieces {pieces} {M}x{N}x{K}"
+                assert_within_bound(fmt, got, ref, mag, what)
+                if first is None:
+                    first = got
+                else:
+                    assert np.array_equal(got, first), f"{what} differs in bits from swap S=1"
+        if pieces == 1:  # tile size alone does not change an element's summation order
+            if unsplit is None:
+                unsplit = first
+            else:
+                assert np.array_equal(first, unsplit), f"tile {tile} differs in bits from tile 256"
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-def test_nt_k_zero_gives_zeros(pg, fmt):
-    A = np.zeros((70, 0), np.uint16)
-    B = np.zeros((90, 0), np.uint16)
+@pytest.mark.parametrize("tile,split", TILINGS)
+def test_nt_k_zero_gives_zeros(pg, fmt, tile, split):
+    with tiling(pg, tile, split):
+        _k_zero(pg, fmt)
+
+
+def _k_zero(pg, fmt):
     for variant, s in VARIANTS:
         dA = torch.zeros((70, 0), dtype=torch.float16 if fmt == "f16" else torch.bfloat16, device="cuda")
         dB = torch.zeros((90, 0), dtype=dA.dtype, device="cuda")
@@ -111,8 +139,14 @@ def test_nt_k_zero_gives_zeros(pg, fmt):
         assert torch.count_nonzero(out).item() == 0
 
 
+@pytest.mark.parametrize("tile,split", TILINGS)
 @pytest.mark.parametrize("variant,stages", VARIANTS)
-def test_nt_closed_forms(pg, variant, stages):
+def test_nt_closed_forms(pg, variant, stages, tile, split):
+    with tiling(pg, tile, split):
+        _closed_forms(pg, variant, stages)
+
+
+def _closed_forms(pg, variant, stages):
     # identity: lhs * I^T = lhs exactly
     K = 384
     A = inputs.f16_uniform1((300, K), 3, 0)
@@ -192,13 +226,23 @@ def test_workload_f16_8192_stage_sweep(pg):
         assert np.array_equal(v, first), f"{k} differs in bits from ws S=1"
 
 
-@pytest.mark.parametrize("variant,stages", [("ws", 4), ("ws", 2), ("swap", 4), ("swap", 2), ("swap", 1)])
-def test_workload_bf16_ragged_4095x1000x1000(pg, variant, stages):
+@pytest.fixture(scope="module")
+def w4():
     M, N, K = 4095, 1000, 1000
     A, B = inputs.make_operands("bf16_nt", M, N, K, inputs.workload_seed(4))
     ref, mag = oracle.gemm_nt("bf16", A, B)
-    got = run_nt(pg, "bf16", variant, A, B, stages)
-    q = pg.pgemm_query("nt_ws" if variant == "ws" else "nt_swap", stages, M, N, K)
+    return A, B, ref, mag
+
+
+@pytest.mark.parametrize("tile", [0, 256])
+@pytest.mark.parametrize("variant,stages", [("ws", 4), ("ws", 2), ("swap", 4), ("swap", 2), ("swap", 1)])
+def test_workload_bf16_ragged_4095x1000x1000(pg, w4, variant, stages, tile):
+    M, N, K = 4095, 1000, 1000
+    A, B, ref, mag = w4
+    with tiling(pg, tile, 0):
+        got = run_nt(pg, "bf16", variant, A, B, stages)
+        q = pg.pgemm_query("nt_ws" if variant == "ws" else "nt_swap", stages, M, N, K)
+    assert q["block_m"] == (tile or 128)
     # report the edges separately: last partial row tile, last partial column tile
     em = (M // q["block_m"]) * q["block_m"]
     en = (N // q["block_n"]) * q["block_n"]
@@ -210,12 +254,48 @@ def test_workload_bf16_ragged_4095x1000x1000(pg, variant, stages):
 def test_workload_f16_skinny_128x8192x16384(pg):
     A, B = inputs.make_operands("f16_nt", 128, 8192, 16384, inputs.workload_seed(5))
     dA, dB = dev_half(A, "f16"), dev_half(B, "f16")
-    outs = {f"ws S={s}": run_nt(pg, "f16", "ws", A, B, s, dA, dB) for s in (2, 3, 4)}
-    outs["swap S=2"] = run_nt(pg, "f16", "swap", A, B, 2, dA, dB)
-    check_sampled("f16", A, B, outs, 5, count=2048)
-    first = outs["ws S=2"]
+    assert pg.pgemm_query("nt_ws", 0, 128, 8192, 16384)["k_split"] == 4  # the planned split
+    outs = {f"ws S={s}": run_nt(pg, "f16", "ws", A, B, s, dA, dB) for s in (1, 2, 3, 4)}
+    outs.update({f"swap S={s}": run_nt(pg, "f16", "swap", A, B, s, dA, dB) for s in (1, 2, 3, 4)})
+    with tiling(pg, 128, 1):
+        unsplit = run_nt(pg, "f16", "ws", A, B, 4, dA, dB)
+    with tiling(pg, 256, 0):
+        large = run_nt(pg, "f16", "swap", A, B, 2, dA, dB)
+    check_sampled("f16", A, B, dict(outs, unsplit=unsplit, large=large), 5, count=2048)
+    first = outs["ws S=1"]
     for k, v in outs.items():
         assert np.array_equal(v, first), k
+    assert np.array_equal(unsplit, large)
+
+
+def test_split_workspace_per_stream_and_growth(pg):
+    # Two streams running K-split products at once each get their own
+    # workspace; a larger split product on a stream grows that stream's.
+    shapes = [(64, 1000, 4096, 2), (100, 700, 8192, 4), (128, 2000, 16384, 8)]
+    data = []
+    for i, (M, N, K, split) in enumerate(shapes):
+        A, B = inputs.make_operands("f16_nt", M, N, K, 4242 + i)
+        data.append((A, B, dev_half(A, "f16"), dev_half(B, "f16"), split))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(2):
+        for i, (A, B, dA, dB, split) in enumerate(data):
+            with tiling(pg, 128, split):
+                o = pg.pgemm_f16_nt_ws(dA, dB, stages=3, stream=streams[(i + rep) % 2])
+                o2 = pg.pgemm_f16_nt(dA, dB, stages=2, stream=streams[(i + rep + 1) % 2])
+                outs.append((i, o, o2))
+    torch.cuda.synchronize()
+    results = {}
+    for i, o, o2 in outs:
+        got, got2 = host_bits(o), host_bits(o2)
+        assert np.array_equal(got, got2)
+        if i in results:
+            assert np.array_equal(got, results[i])
+        results[i] = got
+    for i, (A, B, _, _, split) in enumerate(data):
+        ref, mag = oracle.gemm_nt("f16", A, B)
+        assert_within_bound("f16", results[i], ref, mag, f"split {split}")
 
 
 # ----------------------------------------------------- credit protocol
