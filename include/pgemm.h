@@ -163,6 +163,56 @@ pgemm_status pgemm_set_tiling(int tile, int k_split);
  * needs: without the seeds the first producer wait can never succeed). */
 void pgemm_set_ws_debug(int64_t max_polls, int skip_seed);
 
+/*
+ * Pipeline planner (host only, no HIP call), the rules the library applies
+ * to size each kernel's LDS ring (TileLang ch.22, "pipeline-sync-
+ * multibuffer": §2.2 stage/order validity, §2.4 version count, §3.3 arena
+ * packing).
+ *
+ * pgemm_plan_versions: statements 0 .. n_stmts-1 of a pipelined loop body,
+ * annotated with stage[i] >= 0 and order[i] (all orders distinct), and their
+ * buffer accesses.  The annotation is valid when every buffer a statement
+ * reads that another writes has the writer in an earlier stage, or in the
+ * same stage and earlier in order; else PGEMM_ERR_STAGES.  On success
+ * versions[b] = use - def + 1 for each buffer b (def: earliest stage that
+ * writes it, use: latest stage that reads it), 1 for a buffer the body never
+ * writes, and one less whenever the count is at least 2 but no writer
+ * precedes a reader both in order and in stage.  PGEMM_ERR_SHAPE for
+ * negative counts or indices out of range, PGEMM_ERR_NULL for a missing
+ * array.  The caller owns all arrays.
+ */
+typedef struct {
+  int32_t stmt;   /* statement index */
+  int32_t buffer; /* buffer index */
+  int32_t write;  /* 1: the statement writes the buffer; 0: it reads it */
+} pgemm_access;
+
+pgemm_status pgemm_plan_versions(int32_t n_stmts, const int32_t *stage, const int32_t *order,
+                                 int32_t n_access, const pgemm_access *access,
+                                 int32_t n_buffers, int32_t *versions);
+
+/*
+ * pgemm_plan_arena: packs n buffers, each `versions` copies of `bytes` kept
+ * as one block and live over program points [start, end), into one LDS
+ * arena.  Blocks are placed in order of (start, larger first, index); the
+ * blocks whose interval ended by then return to a sorted, coalesced free
+ * list; a block takes the hole that wastes least after alignment, else new
+ * space at the arena's top (a free hole reaching the top is grown).
+ * Writes offsets[i], the arena size and the sum of all blocks (no reuse).
+ * PGEMM_ERR_SHAPE for bytes < 0, versions < 1, align not a power of two or
+ * start >= end; PGEMM_ERR_NULL for a missing array.
+ */
+typedef struct {
+  int64_t bytes;    /* bytes of one version                     */
+  int32_t versions; /* copies kept                              */
+  int32_t align;    /* alignment in bytes, a power of two       */
+  int32_t start;    /* first program point the buffer is live   */
+  int32_t end;      /* first program point it is dead again     */
+} pgemm_lds_block;
+
+pgemm_status pgemm_plan_arena(int32_t n, const pgemm_lds_block *blocks, int64_t *offsets,
+                              int64_t *arena_bytes, int64_t *no_reuse_bytes);
+
 const char *pgemm_strerror(pgemm_status status);
 int pgemm_abi_version(void);
 

@@ -362,6 +362,10 @@ __global__ void __launch_bounds__(G::THREADS, G::OCC)
       w.template mixed_step<false, 0>(f[1], f[0], lane_a(0), lane_b(0), 0, hi, sw, no_load);
     }
   }
+  // Loads of tiles past the end are still in flight (they read zeros); none
+  // may land after this point, where the ring becomes the staging tile or
+  // the workgroup ends.
+  wait_vmcnt<0>();
   if constexpr (SPLIT) {
     w.store_partial(partial + (int64_t)split * M * ldp, ldp, M, N, m0 + wm * G::WM, n0 + wn * G::WN, lane);
   } else {

@@ -13,6 +13,7 @@
 
 #include "pgemm.h"
 #include "instances.hpp"
+#include "planner.hpp"
 
 // Device-side error word: a credit wait that runs past its poll limit sets
 // bit 0.  One copy per device; the host reaches it through its address.
@@ -61,6 +62,24 @@ struct Plan {
   pgemm_kernel_info info{};
 };
 
+// LDS of an NT instance as the pipeline planner sees it: the K loop is two
+// statements, the fill (stage 0, order 0) writing the ring and the MMA
+// (stage S-1, order 1) reading it, which gives the ring's version count;
+// the ring (live over the loop) and the epilogue staging tile (live after
+// it) are packed into one arena; the credit counters of the
+// producer/consumer kernel follow the arena.
+template <class G>
+int64_t planned_lds() {
+  using namespace planner;
+  const std::vector<int> stage{0, G::S - 1}, order{0, 1};
+  const std::vector<Access> acc{{0, 0, true}, {1, 0, false}};
+  if (!validate(stage, order, acc)) return -1;
+  const int v = versions(0, stage, order, acc);
+  const std::vector<Block> blocks{{(int64_t)v * G::Loader::SLOT_BYTES, 16, 0, 1}, {G::STAGE_BYTES, 16, 1, 2}};
+  std::vector<int64_t> off;
+  return pack(blocks, &off) + (G::P > 0 ? 2 * G::S * 4 : 0);
+}
+
 template <class G>
 void fill_nt(Plan *p, int64_t M, int64_t N) {
   pgemm_kernel_info *i = &p->info;
@@ -71,7 +90,9 @@ void fill_nt(Plan *p, int64_t M, int64_t N) {
   i->producer_waves = G::P;
   i->consumer_waves = G::CW;
   i->threads = G::THREADS;
-  i->lds_bytes = G::LDS_BYTES;
+  // the kernel's static layout must be the planned one
+  const int64_t lds = planned_lds<G>();
+  i->lds_bytes = lds == G::LDS_BYTES ? G::LDS_BYTES : -1;
   i->grid = cdiv(M, G::BM) * cdiv(N, G::BN) * p->split;
   i->k_tiles = cdiv(p->k_chunk, G::BK);
   i->k_split = p->split;
@@ -161,7 +182,7 @@ pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, Plan
     default:
       return PGEMM_ERR_STAGES;
   }
-  if (info->lds_bytes > kLdsLimit) return PGEMM_ERR_LDS;
+  if (info->lds_bytes < 0 || info->lds_bytes > kLdsLimit) return PGEMM_ERR_LDS;
   return PGEMM_OK;
 }
 
@@ -401,6 +422,45 @@ pgemm_status pgemm_set_tiling(int tile, int k_split) {
   if (k_split > 1 && tile != kSmallTile) return PGEMM_ERR_SHAPE;
   g_force_tile.store(tile, std::memory_order_relaxed);
   g_force_split.store(k_split, std::memory_order_relaxed);
+  return PGEMM_OK;
+}
+
+pgemm_status pgemm_plan_versions(int32_t n_stmts, const int32_t *stage, const int32_t *order, int32_t n_access,
+                                 const pgemm_access *access, int32_t n_buffers, int32_t *versions) {
+  if (n_stmts < 0 || n_access < 0 || n_buffers < 0) return PGEMM_ERR_SHAPE;
+  if ((n_stmts > 0 && (!stage || !order)) || (n_access > 0 && !access) || (n_buffers > 0 && !versions))
+    return PGEMM_ERR_NULL;
+  std::vector<int> st(stage, stage + n_stmts), ord(order, order + n_stmts);
+  std::vector<planner::Access> acc;
+  for (int32_t i = 0; i < n_access; ++i) {
+    const pgemm_access &a = access[i];
+    if (a.stmt < 0 || a.stmt >= n_stmts || a.buffer < 0 || a.buffer >= n_buffers) return PGEMM_ERR_SHAPE;
+    acc.push_back(planner::Access{a.stmt, a.buffer, a.write != 0});
+  }
+  for (int32_t i = 0; i < n_stmts; ++i)
+    if (st[(size_t)i] < 0) return PGEMM_ERR_STAGES;
+  if (!planner::validate(st, ord, acc)) return PGEMM_ERR_STAGES;
+  for (int32_t b = 0; b < n_buffers; ++b) versions[b] = planner::versions(b, st, ord, acc);
+  return PGEMM_OK;
+}
+
+pgemm_status pgemm_plan_arena(int32_t n, const pgemm_lds_block *blocks, int64_t *offsets, int64_t *arena_bytes,
+                              int64_t *no_reuse_bytes) {
+  if (n < 0) return PGEMM_ERR_SHAPE;
+  if ((n > 0 && (!blocks || !offsets)) || !arena_bytes || !no_reuse_bytes) return PGEMM_ERR_NULL;
+  std::vector<planner::Block> bl;
+  int64_t sum = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const pgemm_lds_block &b = blocks[i];
+    if (b.bytes < 0 || b.versions < 1 || b.align < 1 || (b.align & (b.align - 1)) || b.start >= b.end)
+      return PGEMM_ERR_SHAPE;
+    bl.push_back(planner::Block{b.bytes * b.versions, b.align, b.start, b.end});
+    sum += b.bytes * b.versions;
+  }
+  std::vector<int64_t> off;
+  *arena_bytes = planner::pack(bl, &off);
+  *no_reuse_bytes = sum;
+  for (int32_t i = 0; i < n; ++i) offsets[i] = off[(size_t)i];
   return PGEMM_OK;
 }
 

@@ -1,0 +1,368 @@
+"""A CPU model of the two ring protocols, for exhaustive interleaving checks.
+
+Test infrastructure: nothing in the library imports it.  It restates, as
+per-wave instruction lists, the schedules that the kernels run:
+
+* single schedule (Croqtile ch.6, "double buffering with swap", with the
+  handles rotated over S slots): every wave issues asynchronous loads of its
+  share of a tile into ring slot t mod S, waits for its own loads, meets the
+  other waves at a workgroup barrier, and reads the slot;
+* producer/consumer (Croqtile ch.6, "1P1C kernel with events" and the credit
+  flow of one stage; Croqtile ch.5, the bootstrap protocol): producers wait
+  for the slot's `empty` credit, write their share, and add one to `full`;
+  consumers seed one `empty` credit per slot, wait for `full`, read the slot
+  and add one to `empty`.  Credits are monotonic counters: round r of a slot
+  waits for (r + 1) x (the number of waves that add to it).
+
+The explorer runs every interleaving of the waves (and, for asynchronous
+loads, every moment at which an issued load may land) by depth-first search
+over distinct states, and reports:
+
+* deadlock: some wave cannot finish and nothing can move;
+* RAW: a read of slot s for tile t while a share of the slot does not hold
+  tile t (not written yet, or overwritten);
+* WAR: a write or a landing load into slot s while another wave is reading
+  the slot;
+* order: a wave that reads tiles other than 0, 1, ..., n_k - 1 in order;
+* leftover (producer/consumer): a tile written that no consumer read.
+
+The hazards are the ones the pages name: the new copy must land in the
+buffer that is not being read (Croqtile ch.6, swap); a missing bootstrap
+credit deadlocks the producer, an early release lets the producer overwrite
+a slot still being read, and both roles must run the same trip count
+(Croqtile ch.6, credit flow; Croqtile ch.5, bootstrap protocol).
+"""
+from __future__ import annotations
+
+import dataclasses
+import random
+from typing import List, Optional
+
+# instruction kinds
+WAIT, ADD, WBEGIN, WEND, RBEGIN, REND, ISSUE, WAITLOADS, BARRIER = range(9)
+
+
+@dataclasses.dataclass
+class Result:
+    deadlock: bool = False
+    raw: bool = False
+    war: bool = False
+    order: bool = False
+    leftover: bool = False
+    states: int = 0
+    example: str = ""
+
+    @property
+    def ok(self) -> bool:
+        return not (self.deadlock or self.raw or self.war or self.order or self.leftover)
+
+
+# ----------------------------------------------------------- programs
+
+
+def ws_programs(S: int, n_k: int, P: int, C: int, *, bootstrap: bool = True, early_release: bool = False,
+                producer_trips: Optional[int] = None, consumer_trips: Optional[int] = None,
+                lookahead: int = 0, no_sync: bool = False):
+    """Producer/consumer: P producers (share p of every slot), C consumers.
+
+    Faults: bootstrap=False drops the consumers' initial `empty` credits; early_release adds to
+    `empty` before the slot's reads finish; *_trips changes one role's trip
+    count; lookahead=1 lets producers run one round ahead of their credits;
+    no_sync drops every wait and credit."""
+    pt = n_k if producer_trips is None else producer_trips
+    ct = n_k if consumer_trips is None else consumer_trips
+    progs = []
+    for p in range(P):
+        prog = []
+        for t in range(pt):
+            s, r = t % S, t // S
+            if not no_sync:
+                prog.append((WAIT, "empty", s, C * (r + 1 - lookahead)))
+            prog.append((WBEGIN, s, t, p))
+            prog.append((WEND, s, t, p))
+            if not no_sync:
+                prog.append((ADD, "full", s))
+        progs.append(prog)
+    for c in range(C):
+        prog = []
+        if bootstrap and not no_sync:
+            for s in range(S):
+                prog.append((ADD, "empty", s))
+        for t in range(ct):
+            s, r = t % S, t // S
+            if not no_sync:
+                prog.append((WAIT, "full", s, P * (r + 1)))
+            if early_release and not no_sync:
+                prog.append((ADD, "empty", s))
+            prog.append((RBEGIN, s, t))
+            prog.append((REND, s, t))
+            if not early_release and not no_sync:
+                prog.append((ADD, "empty", s))
+        progs.append(prog)
+    return progs, P  # shares per slot: one per producer
+
+
+def swap_programs(S: int, n_k: int, W: int, *, skip_barrier: bool = False, skip_wait: bool = False,
+                  refill_before_barrier: bool = False):
+    """Single schedule with W waves, as the kernels run it.
+
+    Each wave's share of a tile is two halves (shares 2w and 2w + 1), issued
+    as asynchronous loads that land later.  S = 1: load, wait, barrier, read,
+    barrier.  S >= 2: the prologue issues tiles 0 .. S-2 and the first half
+    of tile S-1; the head of tile t issues the second half of the refill
+    chosen at the previous barrier (tile S-1 before the loop) and reads tile
+    t; then the wave waits for its own loads of tile t+1, meets the others at
+    the barrier, and issues the first half of tile t+S into tile t's slot.
+    Loads of tiles at or past n_k are issued too (they read zeros in the
+    kernel); before the epilogue the wave waits for all of its loads.
+
+    Faults: skip_barrier drops the per-tile barrier; skip_wait drops the
+    wait for the wave's own loads; refill_before_barrier issues the refill
+    of tile t's slot before the barrier instead of after it."""
+    progs = []
+    for w in range(W):
+        a, b = 2 * w, 2 * w + 1
+        prog = []
+        nb = 0
+        if S == 1:
+            for t in range(n_k):
+                prog += [(ISSUE, 0, t, a), (ISSUE, 0, t, b)]
+                if not skip_wait:
+                    prog.append((WAITLOADS, t))
+                if not skip_barrier:
+                    prog.append((BARRIER, nb)); nb += 1
+                prog += [(RBEGIN, 0, t), (REND, 0, t)]
+                if not skip_barrier:
+                    prog.append((BARRIER, nb)); nb += 1
+            progs.append(prog)
+            continue
+        for j in range(S - 1):
+            prog += [(ISSUE, j % S, j, a), (ISSUE, j % S, j, b)]
+        prog.append((ISSUE, (S - 1) % S, S - 1, a))
+        if not skip_wait:
+            prog.append((WAITLOADS, 0))
+        if not skip_barrier:
+            prog.append((BARRIER, nb)); nb += 1
+        refill = S - 1
+        for t in range(n_k):
+            s = t % S
+            prog.append((ISSUE, refill % S, refill, b))  # second half of the pending refill
+            prog += [(RBEGIN, s, t), (REND, s, t)]
+            if t + 1 < n_k:
+                if refill_before_barrier:
+                    prog.append((ISSUE, (t + S) % S, t + S, a))
+                if not skip_wait:
+                    prog.append((WAITLOADS, t + 1))
+                if not skip_barrier:
+                    prog.append((BARRIER, nb)); nb += 1
+                if not refill_before_barrier:
+                    prog.append((ISSUE, (t + S) % S, t + S, a))
+                refill = t + S
+        prog.append((WAITLOADS, 10 ** 9))  # the epilogue waits for every load
+        progs.append(prog)
+    return progs, 2 * W
+
+
+# ----------------------------------------------------------- explorer
+
+
+class _Explorer:
+    def __init__(self, progs, shares: int, S: int, n_k: int, readers: List[int], max_states: int,
+                 check_leftover: bool = False):
+        self.progs = progs
+        self.shares = shares
+        self.S = S
+        self.n_k = n_k
+        self.readers = readers  # waves whose reads must cover 0..n_k-1 in order
+        self.max_states = max_states
+        self.res = Result()
+        self.seen = set()
+        self.n_waves = len(progs)
+        self.check_leftover = check_leftover
+
+    # state: (pcs, counters, slot tags, shares being written, waves reading,
+    #         loads in flight, tiles read per wave, loads issued per wave)
+    def initial(self):
+        pcs = tuple(0 for _ in self.progs)
+        ctr = (tuple(0 for _ in range(self.S)), tuple(0 for _ in range(self.S)))
+        tags = tuple(tuple(None for _ in range(self.shares)) for _ in range(self.S))
+        writing = tuple(tuple(None for _ in range(self.shares)) for _ in range(self.S))
+        reading = tuple(frozenset() for _ in range(self.S))  # waves reading the slot
+        inflight = frozenset()  # (wave, seq, slot, tile, share)
+        log = tuple(() for _ in self.progs)
+        issued = tuple(0 for _ in self.progs)
+        return (pcs, ctr, tags, writing, reading, inflight, log, issued)
+
+    def flag(self, kind: str, what: str):
+        setattr(self.res, kind, True)
+        if not self.res.example:
+            self.res.example = f"{kind}: {what}"
+
+    def moves(self, st):
+        """Enabled moves: ('wave', w) or ('land', item)."""
+        pcs, ctr, tags, writing, reading, inflight, log, issued = st
+        out = []
+        for w, prog in enumerate(self.progs):
+            pc = pcs[w]
+            if pc >= len(prog):
+                continue
+            ins = prog[pc]
+            k = ins[0]
+            if k == WAIT:
+                which = 0 if ins[1] == "full" else 1
+                if ctr[which][ins[2]] < ins[3]:
+                    continue
+            elif k == WAITLOADS:
+                # all of this wave's loads of tiles <= ins[1] have landed
+                if any(it[0] == w and it[3] <= ins[1] for it in inflight):
+                    continue
+            elif k == BARRIER:
+                # enabled when every wave is at this barrier (or finished)
+                ok = True
+                for v, pv in enumerate(self.progs):
+                    if pcs[v] >= len(pv) or pv[pcs[v]] != (BARRIER, ins[1]):
+                        ok = False
+                        break
+                if not ok:
+                    continue
+            out.append(("wave", w))
+        for it in inflight:
+            out.append(("land", it))
+        return out
+
+    def step(self, st, mv):
+        pcs, ctr, tags, writing, reading, inflight, log, issued = st
+        pcs = list(pcs)
+        if mv[0] == "land":
+            w, seq, s, t, share = mv[1]
+            if reading[s]:
+                self.flag("war", f"load of tile {t} landed in slot {s} while it was read")
+            tags = _set2(tags, s, share, t)
+            inflight = inflight - {mv[1]}
+            return (tuple(pcs), ctr, tags, writing, reading, inflight, log, issued)
+        w = mv[1]
+        ins = self.progs[w][pcs[w]]
+        k = ins[0]
+        if k == BARRIER:
+            # all waves pass together
+            for v in range(self.n_waves):
+                pcs[v] += 1
+            return (tuple(pcs), ctr, tags, writing, reading, inflight, log, issued)
+        pcs[w] += 1
+        if k == ADD:
+            which = 0 if ins[1] == "full" else 1
+            c = list(ctr)
+            row = list(c[which])
+            row[ins[2]] += 1
+            c[which] = tuple(row)
+            ctr = tuple(c)
+        elif k == WBEGIN:
+            _, s, t, share = ins
+            if reading[s]:
+                self.flag("war", f"write of tile {t} into slot {s} while it was read")
+            writing = _set2(writing, s, share, t)
+            tags = _set2(tags, s, share, None)
+        elif k == WEND:
+            _, s, t, share = ins
+            writing = _set2(writing, s, share, None)
+            tags = _set2(tags, s, share, t)
+        elif k == RBEGIN:
+            _, s, t = ins
+            if any(x != t for x in tags[s]) or any(x is not None for x in writing[s]):
+                self.flag("raw", f"read of tile {t} from slot {s} holding {tags[s]}")
+            reading = _set1(reading, s, reading[s] | {w})
+        elif k == REND:
+            _, s, t = ins
+            if any(x != t for x in tags[s]) or any(x is not None for x in writing[s]):
+                self.flag("raw", f"slot {s} changed while tile {t} was read")
+            reading = _set1(reading, s, reading[s] - {w})
+            log = _set1(log, w, log[w] + (t,))
+        elif k == ISSUE:
+            _, s, t, share = ins
+            iss = list(issued)
+            iss[w] += 1
+            issued = tuple(iss)
+            inflight = inflight | {(w, issued[w], s, t, share)}
+        return (tuple(pcs), ctr, tags, writing, reading, inflight, log, issued)
+
+    def finished(self, st):
+        pcs = st[0]
+        return all(pcs[w] >= len(p) for w, p in enumerate(self.progs)) and not st[5]
+
+    def check_final(self, st):
+        log = st[6]
+        for w in self.readers:
+            if log[w] != tuple(range(self.n_k)):
+                self.flag("order", f"wave {w} read tiles {log[w]}")
+        if self.check_leftover:
+            read = set().union(*(set(log[w]) for w in self.readers))
+            for row in st[2]:
+                for t in row:
+                    if t is not None and t not in read:
+                        self.flag("leftover", f"tile {t} written but never read")
+
+    def run(self, exhaustive: bool = True, walks: int = 0, rng: Optional[random.Random] = None,
+            stop_at_first: bool = False):
+        init = self.initial()
+        if exhaustive:
+            stack = [init]
+            self.seen.add(init)
+            while stack and not (stop_at_first and not self.res.ok):
+                st = stack.pop()
+                mv = self.moves(st)
+                if not mv:
+                    if self.finished(st):
+                        self.check_final(st)
+                    else:
+                        self.flag("deadlock", f"stuck at pcs {st[0]}")
+                    continue
+                for m in mv:
+                    nxt = self.step(st, m)
+                    if nxt not in self.seen:
+                        if len(self.seen) >= self.max_states:
+                            raise RuntimeError("state space larger than the explorer's limit")
+                        self.seen.add(nxt)
+                        stack.append(nxt)
+            self.res.states = len(self.seen)
+        for _ in range(walks):
+            st = init
+            while True:
+                mv = self.moves(st)
+                if not mv:
+                    if self.finished(st):
+                        self.check_final(st)
+                    else:
+                        self.flag("deadlock", f"stuck at pcs {st[0]}")
+                    break
+                st = self.step(st, rng.choice(mv))
+            self.res.states += 1
+        return self.res
+
+
+def _set1(tup, i, v):
+    l = list(tup)
+    l[i] = v
+    return tuple(l)
+
+
+def _set2(tup, i, j, v):
+    row = list(tup[i])
+    row[j] = v
+    return _set1(tup, i, tuple(row))
+
+
+def check_ws(S, n_k, P, C, *, exhaustive=True, walks=0, seed=0, max_states=2_000_000, stop_at_first=False,
+             **faults) -> Result:
+    """Explores the producer/consumer protocol (faults: see ws_programs)."""
+    progs, shares = ws_programs(S, n_k, P, C, **faults)
+    readers = list(range(P, P + C))
+    ex = _Explorer(progs, shares, S, n_k, readers, max_states, check_leftover=True)
+    return ex.run(exhaustive, walks, random.Random(seed), stop_at_first)
+
+
+def check_swap(S, n_k, W, *, exhaustive=True, walks=0, seed=0, max_states=2_000_000, stop_at_first=False,
+               **faults) -> Result:
+    """Explores the single schedule (faults: see swap_programs)."""
+    progs, shares = swap_programs(S, n_k, W, **faults)
+    ex = _Explorer(progs, shares, S, n_k, list(range(W)), max_states)
+    return ex.run(exhaustive, walks, random.Random(seed), stop_at_first)

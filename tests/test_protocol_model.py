@@ -1,0 +1,125 @@
+"""The ring protocols in a CPU model (no GPU): both schedules are free of
+deadlock and slot hazards over every interleaving for small sizes, and each
+protocol mistake the pages warn about is caught.
+
+Pins: the pages' own statements (Croqtile ch.6, swap: the new copy lands in
+the buffer not being read; credit flow of one stage: both roles must run
+the same number of iterations, the producer waits for `empty` and the
+consumer for `full`; Croqtile ch.5, bootstrap protocol: without the initial
+`empty` credits the producer waits forever; releasing before the reads are
+done lets the producer overwrite a slot in use), and the kernels' own wait
+constants, checked against the model's wait points.
+"""
+import pytest
+
+from protocol_model import ISSUE, WAITLOADS, check_swap, check_ws, swap_programs
+
+
+# ------------------------------------------------------ correct schedules
+
+@pytest.mark.parametrize("S,n_k,W", [(1, 0, 2), (1, 1, 2), (1, 3, 2), (1, 4, 3),
+                                     (2, 0, 2), (2, 1, 2), (2, 2, 2), (2, 3, 2), (2, 6, 2), (2, 3, 3),
+                                     (3, 1, 2), (3, 2, 2), (3, 4, 2), (4, 1, 2), (4, 3, 2), (4, 4, 2)])
+def test_swap_schedule_safe_in_every_interleaving(S, n_k, W):
+    r = check_swap(S, n_k, W)
+    assert r.ok, r.example
+    assert r.states > 0
+
+
+@pytest.mark.parametrize("S,n_k,W", [(2, 12, 2), (3, 10, 3), (4, 9, 2), (4, 7, 4)])
+def test_swap_schedule_safe_on_random_interleavings(S, n_k, W):
+    r = check_swap(S, n_k, W, exhaustive=False, walks=300, seed=S * 100 + n_k)
+    assert r.ok, r.example
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("n_k", [0, 1, 2, 3, 5, 6])
+@pytest.mark.parametrize("P,C", [(1, 1), (1, 2), (2, 2), (1, 4)])
+def test_ws_protocol_safe_in_every_interleaving(S, n_k, P, C):
+    if P * C >= 4 and n_k >= 5 and S >= 3:
+        pytest.skip("covered by the random walks below")
+    r = check_ws(S, n_k, P, C)
+    assert r.ok, r.example
+
+
+@pytest.mark.parametrize("S,n_k,P,C", [(4, 16, 4, 8), (2, 20, 4, 8), (3, 12, 2, 4), (1, 8, 4, 8)])
+def test_ws_protocol_safe_on_random_interleavings(S, n_k, P, C):
+    # the kernels' own role counts: 4 producers and 8 consumers (256 x 256
+    # tiles), 2 and 4 (128 x 128 tiles)
+    r = check_ws(S, n_k, P, C, exhaustive=False, walks=200, seed=S + n_k)
+    assert r.ok, r.example
+
+
+def test_kernel_wait_constants_match_the_model():
+    # nt_swap_kernel waits with s_waitcnt vmcnt(N) for static N: (S-2)*PER
+    # before each barrier and (S-2)*PER + PER/2 in the prologue, PER loads
+    # per wave and tile issued in two halves.  In the model one ISSUE is one
+    # half, so at each wait for "tiles <= u landed" exactly 2(S-2) issues
+    # (2(S-2) + 1 in the prologue) of later tiles may still be in flight, and
+    # every issue of a tile <= u comes before them (loads complete in order).
+    for S in (2, 3, 4):
+        for n_k in (1, 2, 5, 9):
+            prog = swap_programs(S, n_k, 1)[0][0]
+            waits = [i for i, ins in enumerate(prog) if ins[0] == WAITLOADS and ins[1] < 10 ** 9]
+            assert waits
+            for j, i in enumerate(waits):
+                u = prog[i][1]
+                issues = [ins for ins in prog[:i] if ins[0] == ISSUE]
+                later = [ins for ins in issues if ins[2] > u]
+                expect = 2 * (S - 2) + (1 if j == 0 else 0)
+                assert len(later) == expect, (S, n_k, u)
+                first_later = next((k for k, ins in enumerate(issues) if ins[2] > u), len(issues))
+                assert all(ins[2] > u for ins in issues[first_later:])
+
+
+# ------------------------------------------------------ planted mistakes
+
+def test_missing_bootstrap_deadlocks():
+    for S, P, C in [(1, 1, 1), (2, 1, 2), (4, 2, 2)]:
+        r = check_ws(S, 4, P, C, bootstrap=False)
+        assert r.deadlock and not r.raw and not r.war
+
+
+def test_release_before_reads_finish_lets_the_producer_overwrite():
+    for S in (1, 2, 3):
+        r = check_ws(S, S + 2, 1, 2, early_release=True)
+        assert r.war
+
+
+def test_producer_running_one_round_ahead_overwrites():
+    for S in (1, 2, 3):
+        r = check_ws(S, S + 2, 1, 2, lookahead=1)
+        assert r.raw or r.war
+
+
+@pytest.mark.parametrize("who,trips,expect", [
+    ("consumer_trips", 3, "order"),     # a tile is left unread
+    ("consumer_trips", 5, "deadlock"),  # a consumer waits for a tile never produced
+    ("producer_trips", 3, "deadlock"),
+    ("producer_trips", 5, "leftover"),  # a tile produced that nobody reads
+    ("producer_trips", 8, "deadlock"),  # ... and past the ring's slack the producer blocks
+])
+def test_mismatched_trip_counts(who, trips, expect):
+    r = check_ws(2, 4, 1, 2, **{who: trips})
+    assert getattr(r, expect), r.example
+    assert not r.ok
+
+
+def test_no_synchronisation_races():
+    assert not check_ws(2, 4, 1, 2, no_sync=True).ok
+    assert not check_swap(2, 3, 2, skip_barrier=True, skip_wait=True, stop_at_first=True).ok
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+def test_swap_without_barrier_or_wait_is_caught(S):
+    n_k = S + 1
+    assert check_swap(S, n_k, 2, skip_barrier=True, stop_at_first=True).raw
+    assert check_swap(S, n_k, 2, skip_wait=True, stop_at_first=True).raw
+
+
+@pytest.mark.parametrize("S", [2, 3, 4])
+def test_refill_before_the_barrier_is_caught(S):
+    # the refill of tile t's slot issued before every wave has finished
+    # reading tile t: the copy may land in the buffer still being read
+    r = check_swap(S, S + 1, 2, refill_before_barrier=True, stop_at_first=True)
+    assert r.raw or r.war
