@@ -156,34 +156,6 @@ struct SlotLoader {
 #pragma unroll
     for (int i = 0; i < COUNT; ++i) load_one(slot, t, first + i, i % PAR);
   }
-
-  // Register path, same granule map: `fetch` brings the 16 bytes that lane l
-  // of instruction j would write into registers, `put` writes them to the
-  // slot (lane l of instruction j -> granule 64 j + l, conflict-free).
-  template <int COUNT>
-  __device__ __forceinline__ void fetch(u32x4 (&r)[COUNT], int t, int first, int lane) const {
-    const int k0 = t * BK;
-    const bool whole = k0 + BK <= klen;
-#pragma unroll
-    for (int i = 0; i < COUNT; ++i) {
-      const int j = first + i;
-      const bool is_a = j < A_INSTR;
-      const int jj = is_a ? j : j - A_INSTR;
-      const int row = jj * (kWave / CPR) + lane / CPR;
-      const int chunk = (lane % CPR) ^ Row::swz(row);
-      const int kc = k0 + chunk * 8;
-      uint32_t off = ((uint32_t)row * (uint32_t)pitch + (uint32_t)kc) * 2u;
-      if (!whole && kc >= klen) off = kOobOffset;
-      r[i] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? ra : rb, (int)off, 0, 0);
-    }
-  }
-
-  template <int COUNT>
-  __device__ __forceinline__ static void put(const u32x4 (&r)[COUNT], char *slot, int first, int lane) {
-#pragma unroll
-    for (int i = 0; i < COUNT; ++i)
-      *reinterpret_cast<u32x4 *>(slot + (first + i) * (kWave * 16) + lane * 16) = r[i];
-  }
 };
 
 // Load issuers for mixed_step: call i issues instruction first + i of the
@@ -234,15 +206,6 @@ struct NtGeom {
   static constexpr int STAGE_BYTES = BM * Staging<BN>::PITCH;
   static constexpr int CTR_OFFSET = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
   static constexpr int LDS_BYTES = CTR_OFFSET + (P > 0 ? 2 * S * 4 : 0);
-  // Producer register staging: each producer wave holds its share of the
-  // next RBUF K tiles in VGPRs (global -> VGPR while the tile's ring slot is
-  // still being read, VGPR -> LDS once the slot's `empty` credit arrives).
-  // Every wave of the kernel is allocated the consumers' register budget
-  // anyway, so these buffers cost nothing and add RBUF tiles of loads in
-  // flight beyond what the LDS ring holds.
-  static constexpr int RBUF = P > 0 ? (BK == 64 ? 2 : 4) : 0;
-  static_assert(P == 0 || RBUF * PER_LOADER * 4 <= 128, "staging fits the producer's registers");
-  static_assert(P == 0 || RBUF * PER_LOADER < 64, "staged loads fit the 6-bit vmcnt");
   static_assert(Loader::INSTR % LOADERS == 0, "loads split evenly");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave blocks are whole 32x32 MFMA tiles");
   static_assert(S <= 4, "vmcnt wait table covers three tiles in flight");
@@ -427,23 +390,33 @@ __global__ void __launch_bounds__(G::THREADS)
     Loader ld;
     ld.init(lhs, rhs, M, N, K, kb, klen, m0, n0);
     const int first = (wave - C) * G::PER_LOADER;
-    constexpr int R = G::RBUF;
-    u32x4 buf[R][G::PER_LOADER];
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-      if (j < n_k) ld.fetch(buf[j], j, first, lane);  // prologue: R tiles in flight
-    for (int t0 = 0; t0 < n_k; t0 += R) {
-#pragma unroll
-      for (int b = 0; b < R; ++b) {
-        const int t = t0 + b;
-        if (t >= n_k) break;
-        const int s = t % S;
-        const uint32_t round = (uint32_t)(t / S);
-        credit_wait(&empty[s], (uint32_t)C * (round + 1u), max_polls, err);  // slot free
-        Loader::put(buf[b], slot_ptr(s), first, lane);  // waits for tile t's loads only
-        wait_lgkmcnt0();                                 // the slot holds tile t
-        credit_trigger(&full[s]);
-        if (t + R < n_k) ld.fetch(buf[b], t + R, first, lane);  // refill the register stage
+    // The loads of tile t go straight into its slot (direct to LDS) once
+    // the slot's `empty` credit arrives; `full` of tile t is triggered after
+    // the loads of tile t + LAG are issued, when its own have landed.  LAG =
+    // S - 2 keeps the consumers fed: the tile they need next is complete
+    // once the producer holds the credit of the slot they just released.
+    constexpr int PER = G::PER_LOADER;
+    constexpr int LAG = S >= 2 ? S - 2 : 0;
+    static_assert((LAG + 1) * PER < 64, "loads in flight fit the 6-bit vmcnt");
+    for (int t = 0; t < n_k; ++t) {
+      const int s = t % S;
+      credit_wait(&empty[s], (uint32_t)C * ((uint32_t)(t / S) + 1u), max_polls, err);
+      ld.template load<PER>(slot_ptr(s), t, first, lane);
+      if (t >= LAG) {
+        wait_vmcnt<LAG * PER>();  // tile t - LAG landed
+        credit_trigger(&full[(t - LAG) % S]);
+      }
+    }
+    if constexpr (LAG >= 2) {
+      if (n_k >= 2) {
+        wait_vmcnt<PER>();
+        credit_trigger(&full[(n_k - 2) % S]);
+      }
+    }
+    if constexpr (LAG >= 1) {
+      if (n_k >= 1) {
+        wait_vmcnt<0>();
+        credit_trigger(&full[(n_k - 1) % S]);
       }
     }
   }

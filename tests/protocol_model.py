@@ -9,7 +9,8 @@ per-wave instruction lists, the schedules that the kernels run:
   other waves at a workgroup barrier, and reads the slot;
 * producer/consumer (Croqtile ch.6, "1P1C kernel with events" and the credit
   flow of one stage; Croqtile ch.5, the bootstrap protocol): producers wait
-  for the slot's `empty` credit, write their share, and add one to `full`;
+  for the slot's `empty` credit, load their share asynchronously, and add
+  one to `full` once the loads have landed;
   consumers seed one `empty` credit per slot, wait for `full`, read the slot
   and add one to `empty`.  Credits are monotonic counters: round r of a slot
   waits for (r + 1) x (the number of waves that add to it).
@@ -62,15 +63,22 @@ class Result:
 
 def ws_programs(S: int, n_k: int, P: int, C: int, *, bootstrap: bool = True, early_release: bool = False,
                 producer_trips: Optional[int] = None, consumer_trips: Optional[int] = None,
-                lookahead: int = 0, no_sync: bool = False):
+                lookahead: int = 0, no_sync: bool = False, lag: Optional[int] = None):
     """Producer/consumer: P producers (share p of every slot), C consumers.
 
-    Faults: bootstrap=False drops the consumers' initial `empty` credits; early_release adds to
-    `empty` before the slot's reads finish; *_trips changes one role's trip
-    count; lookahead=1 lets producers run one round ahead of their credits;
-    no_sync drops every wait and credit."""
+    As in the kernel, a producer issues its share of tile t as an
+    asynchronous load once slot t mod S has its `empty` credit, and adds to
+    `full` of tile t - lag after waiting for that tile's loads (lag = S - 2,
+    at least 0); the last `lag` tiles are completed after the loop.
+
+    Faults: bootstrap=False drops the consumers' initial `empty` credits;
+    early_release adds to `empty` before the slot's reads finish; *_trips
+    changes one role's trip count; lookahead=1 lets producers run one round
+    ahead of their credits; lag sets another lag; no_sync drops every wait
+    and credit."""
     pt = n_k if producer_trips is None else producer_trips
     ct = n_k if consumer_trips is None else consumer_trips
+    lg = max(S - 2, 0) if lag is None else lag
     progs = []
     for p in range(P):
         prog = []
@@ -78,10 +86,15 @@ def ws_programs(S: int, n_k: int, P: int, C: int, *, bootstrap: bool = True, ear
             s, r = t % S, t // S
             if not no_sync:
                 prog.append((WAIT, "empty", s, C * (r + 1 - lookahead)))
-            prog.append((WBEGIN, s, t, p))
-            prog.append((WEND, s, t, p))
-            if not no_sync:
-                prog.append((ADD, "full", s))
+            prog.append((ISSUE, s, t, p))
+            if not no_sync and t >= lg:
+                prog.append((WAITLOADS, t - lg))
+                prog.append((ADD, "full", (t - lg) % S))
+        if not no_sync:
+            for t in range(max(pt - lg, 0), pt):
+                prog.append((WAITLOADS, t))
+                prog.append((ADD, "full", t % S))
+        prog.append((WAITLOADS, 10 ** 9))
         progs.append(prog)
     for c in range(C):
         prog = []

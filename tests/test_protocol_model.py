@@ -105,6 +105,16 @@ def test_mismatched_trip_counts(who, trips, expect):
     assert not r.ok
 
 
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+def test_producer_lag(S):
+    # full of tile t may trail its loads by up to S - 1 tiles; at S tiles the
+    # producer waits for a slot the consumers can only free after that full
+    for lag in range(S):
+        assert check_ws(S, S + 2, 1, 2, lag=lag, exhaustive=S < 4, walks=0 if S < 4 else 300).ok
+    r = check_ws(S, S + 2, 1, 2, lag=S)
+    assert r.deadlock
+
+
 def test_no_synchronisation_races():
     assert not check_ws(2, 4, 1, 2, no_sync=True).ok
     assert not check_swap(2, 3, 2, skip_barrier=True, skip_wait=True, stop_at_first=True).ok
