@@ -112,6 +112,8 @@ struct SlotLoader {
   __amdgpu_buffer_rsrc_t ra, rb;
   int pitch;  // elements per row of lhs and rhs (the full K)
   int klen;   // K extent this workgroup reads, from column kb on
+  int nk;     // K tiles in that extent
+  int rot;    // the workgroup's K tiles are visited from tile `rot` on, wrapping
   uint32_t lane_off[PAR];  // (l / CPR) * row bytes + chunk * 16, per parity
   int lane_k[PAR];         // chunk * 8: the lane's first k within the tile
 
@@ -120,9 +122,11 @@ struct SlotLoader {
   // row past the matrix edge is out of range while every in-matrix element
   // of the K range is inside.
   __device__ __forceinline__ void init(const uint16_t *lhs, const uint16_t *rhs, int M, int N, int K, int kb,
-                                       int klen_, int m0, int n0) {
+                                       int klen_, int m0, int n0, int rot_ = 0) {
     pitch = K;
     klen = klen_;
+    nk = (klen + BK - 1) / BK;
+    rot = rot_;
     const int rows_a = M - m0 < BM ? M - m0 : BM;
     const int rows_b = N - n0 < BN ? N - n0 : BN;
     ra = make_rsrc(lhs + (int64_t)m0 * K + kb, ((uint32_t)rows_a * (uint32_t)K - (uint32_t)kb) * 2u);
@@ -136,14 +140,20 @@ struct SlotLoader {
     }
   }
 
-  // Instruction j of the slot for K tile t (lane l -> granule 64 j + l);
-  // p = j mod PAR, passed as a constant (every caller's first instruction is
-  // a multiple of PAR, as is A_INSTR) so that the per-lane arrays stay in
-  // registers.
+  // Instruction j of the slot for the t-th K tile of the sequence (lane l ->
+  // granule 64 j + l); p = j mod PAR, passed as a constant (every caller's
+  // first instruction is a multiple of PAR, as is A_INSTR) so that the
+  // per-lane arrays stay in registers.  The t-th tile is K tile
+  // (t + rot) mod nk; t >= nk (issued past the end) stays out of range.
   __device__ __forceinline__ void load_one(char *slot, int t, int j, int p) const {
     const bool is_a = j < A_INSTR;
     const int jj = is_a ? j : j - A_INSTR;
-    const int k0 = t * BK;
+    int kt = t;
+    if (t < nk) {
+      kt = t + rot;
+      if (kt >= nk) kt -= nk;
+    }
+    const int k0 = kt * BK;
     uint32_t voff = lane_off[p] + (uint32_t)(jj * RPI) * (uint32_t)pitch * 2u;
     if (lane_k[p] >= klen - k0) voff = kOobOffset;  // chunk past K (every lane, past the last tile)
     load_lds_x4(is_a ? ra : rb, slot + j * (kWave * 16), voff, (uint32_t)k0 * 2u);
@@ -170,6 +180,20 @@ struct RefillLoads {
 struct NoLoads {
   __device__ __forceinline__ void operator()(int) const {}
 };
+
+// First K tile a workgroup visits.  A K-split product streams its operands
+// from HBM, and when all workgroups walk K in step, every one requests the
+// same 128-byte column window of rows 32 KiB apart, which crowds a few HBM
+// channels (4.1 TB/s for that pattern on its own, 6.3 TB/s with staggered
+// starts).  Split plans therefore start each output tile at its own K tile
+// and wrap around; the order depends on the tile only, so every variant and
+// stage count still gives the same bits for a given plan.  Unsplit plans
+// keep increasing k.
+template <bool SPLIT>
+__device__ __forceinline__ int k_rotation(int bm, int bn, int n_k) {
+  if (!SPLIT || n_k <= 1) return 0;
+  return (int)(((int64_t)bm * 17 + bn) % n_k);
+}
 
 // Workgroup barrier that also orders this wave's LDS accesses before it.
 __device__ __forceinline__ void lds_barrier() {
@@ -254,11 +278,11 @@ __global__ void __launch_bounds__(G::THREADS, G::OCC)
   const int kb = split * k_chunk;
   const int klen = K - kb < k_chunk ? K - kb : k_chunk;
 
+  const int n_k = klen > 0 ? (klen + G::BK - 1) / G::BK : 0;
   Loader ld;
-  ld.init(lhs, rhs, M, N, K, kb, klen, m0, n0);
+  ld.init(lhs, rhs, M, N, K, kb, klen, m0, n0, k_rotation<SPLIT>(bm, bn, n_k));
   W w;
   w.zero();
-  const int n_k = klen > 0 ? (klen + G::BK - 1) / G::BK : 0;
   auto slot_ptr = [&](int s) { return smem + s * Loader::SLOT_BYTES; };
   const int first = wave * G::PER_LOADER;
   const int r = lane & 31, hi = lane >> 5, sw = Row::swz(r);
@@ -388,7 +412,7 @@ __global__ void __launch_bounds__(G::THREADS)
   } else {
     // ---------------------------------------------------------- producer
     Loader ld;
-    ld.init(lhs, rhs, M, N, K, kb, klen, m0, n0);
+    ld.init(lhs, rhs, M, N, K, kb, klen, m0, n0, k_rotation<SPLIT>(bm, bn, n_k));
     const int first = (wave - C) * G::PER_LOADER;
     // The loads of tile t go straight into its slot (direct to LDS) once
     // the slot's `empty` credit arrives; `full` of tile t is triggered after

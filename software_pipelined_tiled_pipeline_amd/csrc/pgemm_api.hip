@@ -27,7 +27,7 @@ constexpr int kLdsLimit = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 // Buffer offsets inside a 256-row panel must stay below 2^31 bytes.
 constexpr int64_t kMaxKNt = (int64_t)1 << 22;
-constexpr int kGroupM = 8;
+constexpr int kGroupM = 4;
 constexpr uint32_t kDefaultPolls = 1u << 24;
 
 std::atomic<uint32_t> g_max_polls{kDefaultPolls};
