@@ -8,8 +8,11 @@ generator.  A step is one GEMM call of the producer/consumer kernel
 finds fastest; the single-schedule kernel is swept too and reported beside it.
 
 Prints one JSON line (rank 0) with TFLOP/s, the roofline position of the
-kernel (average launch time from HIP events on the launch stream), and the
-CPU oracle timed on a bounded sample of the same product.
+kernel (average launch time from HIP events on the launch stream) beside the
+MFMA-only rate the chip sustains under its power limit (libpgemm_probe.so),
+and the CPU oracle timed on a bounded sample of the same product.  Other
+workloads (--workload): 4096^3, the ragged bf16 4095 x 1000 x 1000 and the
+skinny 128 x 8192 x 16384 product (reported against the HBM roofline).
 """
 from __future__ import annotations
 
@@ -28,10 +31,11 @@ PEAK_F16_TFLOPS = 2516.6   # 256 CUs x 4096 flop/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
 
 WORKLOADS = {
-    # name: (M, N, K, seed workload index)
-    "f16_nt_8192": (8192, 8192, 8192, 3),
-    "f16_nt_4096": (4096, 4096, 4096, 2),
-    "f16_nt_skinny": (128, 8192, 16384, 5),
+    # name: (M, N, K, seed workload index, element type)
+    "f16_nt_8192": (8192, 8192, 8192, 3, "f16"),
+    "f16_nt_4096": (4096, 4096, 4096, 2, "f16"),
+    "bf16_nt_ragged": (4095, 1000, 1000, 4, "bf16"),
+    "f16_nt_skinny": (128, 8192, 16384, 5, "f16"),
 }
 
 
@@ -64,25 +68,43 @@ def recorded_traffic(kernel: str, workload: str, stages: int):
 
 
 def time_launches(fn, reps, stream):
-    """Per-launch durations (ms) from HIP events on the launch stream."""
+    """Average duration (ms) of `reps` back-to-back launches: HIP events on
+    the launch stream before the first and after the last."""
     import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in ev:
-        e0.record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
         fn()
-        e1.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    return [e0.elapsed_time(e1) for e0, e1 in ev]
+    return e0.elapsed_time(e1) / reps
 
 
-def cpu_baseline(A, B, M, N, K, budget_s: float):
+def mfma_ceiling():
+    """MFMA-only rate and shader clock from libpgemm_probe.so (no memory
+    traffic), on random and on zero operands; None if the probe fails."""
+    import ctypes
+    path = os.path.join(ROOT, "software_pipelined_tiled_pipeline_amd", "libpgemm_probe.so")
+    P = ctypes.CDLL(path)
+    f = P.pgemm_probe_mfma
+    f.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    out = {}
+    for name, zero in (("random_operands", 0), ("zero_operands", 1)):
+        t, g = ctypes.c_double(), ctypes.c_double()
+        if f(zero, 4000, ctypes.byref(t), ctypes.byref(g)) != 0:
+            return None
+        out[name] = {"tflops": round(t.value, 1), "sclk_ghz": round(g.value, 3)}
+    return out
+
+
+def cpu_baseline(fmt, A, B, M, N, K, budget_s: float):
     """The oracle, as it stands, on a leading block of output rows."""
     import oracle
     rows = 2
     t = 0.0
     while True:
         t0 = time.perf_counter()
-        oracle.gemm_nt("f16", A[:rows], B)
+        oracle.gemm_nt(fmt, A[:rows], B)
         t = time.perf_counter() - t0
         if t * 4 > budget_s or rows * 4 > M:
             break
@@ -135,13 +157,14 @@ def main():
     from software_pipelined_tiled_pipeline_amd import inputs, pgemm
 
     pgemm.lib()  # fails loudly if the HIP library is missing
-    M, N, K, widx = WORKLOADS[args.workload]
+    M, N, K, widx, fmt = WORKLOADS[args.workload]
+    kind, tdt = ("f16_nt", torch.float16) if fmt == "f16" else ("bf16_nt", torch.bfloat16)
     log(f"[bench] generating {args.workload} operands {M}x{N}x{K}")
-    A, B = inputs.make_operands("f16_nt", M, N, K, inputs.workload_seed(widx))
+    A, B = inputs.make_operands(kind, M, N, K, inputs.workload_seed(widx))
     dev = torch.device("cuda:0")
-    dA = torch.from_numpy(A.view(np.int16)).to(dev).view(torch.float16)
-    dB = torch.from_numpy(B.view(np.int16)).to(dev).view(torch.float16)
-    out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    dA = torch.from_numpy(A.view(np.int16)).to(dev).view(tdt)
+    dB = torch.from_numpy(B.view(np.int16)).to(dev).view(tdt)
+    out = torch.empty((M, N), dtype=tdt, device=dev)
     stream = torch.cuda.current_stream()
     flops = 2.0 * M * N * K
     # The skinny product streams a 256 MiB rhs, about the size of the
@@ -149,9 +172,9 @@ def main():
     # a launch cannot be served from what the previous one left in the cache.
     sets = [(A, B, dA, dB)]
     if args.workload == "f16_nt_skinny":
-        A2, B2 = inputs.make_operands("f16_nt", M, N, K, inputs.workload_seed(widx) + 1)
-        sets.append((A2, B2, torch.from_numpy(A2.view(np.int16)).to(dev).view(torch.float16),
-                     torch.from_numpy(B2.view(np.int16)).to(dev).view(torch.float16)))
+        A2, B2 = inputs.make_operands(kind, M, N, K, inputs.workload_seed(widx) + 1)
+        sets.append((A2, B2, torch.from_numpy(A2.view(np.int16)).to(dev).view(tdt),
+                     torch.from_numpy(B2.view(np.int16)).to(dev).view(tdt)))
     turn = [0]
 
     def operands():
@@ -159,49 +182,67 @@ def main():
         turn[0] += 1
         return t, sets[t][2], sets[t][3]
 
-    fns = {"ws": pgemm.pgemm_f16_nt_ws, "swap": pgemm.pgemm_f16_nt}
+    # Launches go straight to the C ABI with the pointers and the stream
+    # handle resolved once, so that host-side argument marshalling does not
+    # show up in the timing of short kernels.
+    import ctypes
+    L = pgemm.lib()
+    names = {"ws": f"pgemm_{fmt}_nt_ws", "swap": f"pgemm_{fmt}_nt"}
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    ptrs = [(ctypes.c_void_p(x[2].data_ptr()), ctypes.c_void_p(x[3].data_ptr())) for x in sets]
+    optr = ctypes.c_void_p(out.data_ptr())
+
+    def launcher(variant, s):
+        f = getattr(L, names[variant])
+
+        def call():
+            t, _, _ = operands()
+            st = f(ptrs[t][0], ptrs[t][1], optr, M, N, K, s, sptr)
+            if st != 0:
+                raise pgemm.PgemmError(st, names[variant])
+            return t
+        return call
+
+    # bring the clocks to their sustained state before anything is timed
+    time_launches(launcher(args.variant, 0), 30, stream)
     sweep = {}
     for variant, stage_set in (("ws", (1, 2, 3, 4)), ("swap", (1, 2, 3, 4))):
         for s in stage_set:
-            f = fns[variant]
-            call = lambda f=f, s=s: f(*operands()[1:], out=out, stages=s)
-            time_launches(call, 2, stream)
-            ms = float(np.median(time_launches(call, 5, stream)))
+            call = launcher(variant, s)
+            time_launches(call, 3, stream)
+            ms = time_launches(call, 10, stream)
             sweep[f"{variant} S={s}"] = round(flops / (ms * 1e-3) / 1e12, 1)
             log(f"[bench] sweep {variant} S={s}: {ms * 1e3:.1f} us, {sweep[f'{variant} S={s}']} TFLOP/s")
     stages = args.stages
     if stages == 0:
         cands = {k: v for k, v in sweep.items() if k.startswith(args.variant + " ")}
         stages = int(max(cands, key=cands.get).split("S=")[1])
-    fn = fns[args.variant]
+    timed = launcher(args.variant, stages)
     last = [0]
 
     def step():
-        t, a, b = operands()
-        last[0] = t
-        fn(a, b, out=out, stages=stages)
+        last[0] = timed()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps of {args.variant} S={stages}")
     t0 = time.perf_counter()
-    durs = time_launches(step, args.steps, stream)
+    kern_ms = time_launches(step, args.steps, stream)
     t1 = time.perf_counter()
     wall = t1 - t0
     if pgemm.pgemm_sync_status() != 0:
         raise RuntimeError("a credit wait gave up during the timed region")
     value = flops * args.steps / wall / 1e12
-    kern_ms = float(np.mean(durs))
     achieved = flops / (kern_ms * 1e-3) / 1e12
 
     # spot check of the timed output against the oracle
     import oracle
     rng = np.random.default_rng(123)
     mi, ni = rng.integers(0, M, 256), rng.integers(0, N, 256)
-    ref, mag = oracle.gemm_nt_entries("f16", sets[last[0]][0], sets[last[0]][1], mi, ni)
+    ref, mag = oracle.gemm_nt_entries(fmt, sets[last[0]][0], sets[last[0]][1], mi, ni)
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)[mi, ni]
-    bad, worst = oracle.check_nt("f16", got, ref, mag)
+    bad, worst = oracle.check_nt(fmt, got, ref, mag)
     if bad:
         raise RuntimeError(f"timed output fails the oracle on {bad} of 256 sampled elements")
 
@@ -209,7 +250,7 @@ def main():
     traffic = recorded_traffic(kname, args.workload, stages)
     result = {
         "metric": "TFLOP/s (and % of MFMA peak) for f16 NT GEMM 8192^3, 1 MI355X"
-        if args.workload == "f16_nt_8192" else f"TFLOP/s for f16 NT GEMM {M}x{N}x{K}, 1 MI355X",
+        if args.workload == "f16_nt_8192" else f"TFLOP/s for {fmt} NT GEMM {M}x{N}x{K}, 1 MI355X",
         "value": round(value, 1),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -219,10 +260,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": fmt,
         "data": "synthetic",
         "config": {
-            "workload": f"f16 NT GEMM M={M} N={N} K={K}, operands uniform[-1,1), fp32 accumulation, "
+            "workload": f"{fmt} NT GEMM M={M} N={N} K={K}, operands "
+                        f"{'uniform[-1,1)' if fmt == 'f16' else 'normal(0,1)'}, fp32 accumulation, "
                         f"{'producer/consumer credits' if args.variant == 'ws' else 'single-schedule swap'}",
             "M": M, "N": N, "K": K,
             "variant": args.variant,
@@ -242,6 +284,13 @@ def main():
             "kernel_avg_us": round(kern_ms * 1e3, 2),
         },
     }
+    if args.workload != "f16_nt_skinny":
+        ceiling = mfma_ceiling()
+        if ceiling:
+            # what the chip sustains under its power limit with no memory
+            # traffic at all: context for `frac`, whose peak is the nominal one
+            ceiling["frac_of_random_operand_ceiling"] = round(achieved / ceiling["random_operands"]["tflops"], 4)
+            result["roofline"]["mfma_only_ceiling"] = ceiling
     if args.workload == "f16_nt_skinny":
         alg_bytes = (M * K + N * K + M * N) * 2
         result["roofline"].update({
@@ -249,7 +298,7 @@ def main():
             "unit": "GB/s", "frac": round(alg_bytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of the same product")
-        result["cpu_baseline"] = cpu_baseline(A, B, M, N, K, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(fmt, A, B, M, N, K, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

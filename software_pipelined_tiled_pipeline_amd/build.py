@@ -9,6 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "pgemm_api.hip")
 LIB = os.path.join(HERE, "libpgemm.so")
+PROBE_SRC = os.path.join(HERE, "csrc", "probe_mfma.hip")
+PROBE_LIB = os.path.join(HERE, "libpgemm_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -24,9 +26,15 @@ HIPCC_FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
+    """Builds libpgemm.so and the measurement aid libpgemm_probe.so."""
+    _compile(PROBE_SRC, PROBE_LIB, verbose)
+    return _compile(SRC, LIB, verbose)
+
+
+def _compile(src: str, lib: str, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, SRC, "-o", tmp]
+    tmp = lib + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, src, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"
     msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l and l.strip()]
@@ -34,8 +42,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -22,8 +22,8 @@ def L():
     return pgemm.lib()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pgemm_\w+)\s*\(", text)))
 
@@ -33,6 +33,21 @@ def test_exports_every_declared_symbol(L):
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_probe_library_exports_its_header():
+    lib = os.path.join(os.path.dirname(pgemm.LIB_PATH), "libpgemm_probe.so")
+    P = ctypes.CDLL(lib)
+    names = declared_functions(os.path.join(ROOT, "include", "pgemm_probe.h"))
+    assert names == ["pgemm_probe_mfma"]
+    for n in names:
+        assert hasattr(P, n), n
+    # argument errors are reported before any HIP call
+    f = P.pgemm_probe_mfma
+    f.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    t, g = ctypes.c_double(), ctypes.c_double()
+    assert f(0, 0, ctypes.byref(t), ctypes.byref(g)) == 1
+    assert f(0, 100, None, ctypes.byref(g)) == 1
 
 
 def test_version_and_messages(L):
