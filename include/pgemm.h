@@ -133,7 +133,7 @@ typedef struct {
   int64_t grid;                      /* workgroups launched (all pieces)   */
   int64_t k_tiles;                   /* K tiles per workgroup (per piece)  */
   int32_t k_split;                   /* K pieces; 1 = no split             */
-  int32_t reserved;                  /* 0                                  */
+  int32_t persistent;                /* 1: persistent schedule (see below) */
   int64_t workspace_bytes;           /* fp32 workspace of a split, else 0  */
 } pgemm_kernel_info;
 
@@ -156,6 +156,18 @@ pgemm_status pgemm_sync_status(void *stream);
  * PGEMM_ERR_SHAPE for any other combination (nothing changes).  Not meant
  * to be changed while other threads launch. */
 pgemm_status pgemm_set_tiling(int tile, int k_split);
+
+/* Tuning and test hook: the schedule of later producer/consumer calls
+ * without a K split.  mode 0: planned (the per-tile kernel: the persistent
+ * one measured no faster on these workloads), 1: never, 2: always.  The persistent kernel
+ * launches at most 256 x (workgroups that fit a CU's LDS, at most 2)
+ * workgroups; each strides over the output tiles (tile_iter * grid +
+ * block, guarded by the tile count; Croqtile ch.5, "persistent scheduling
+ * and the if guard"), its producers streaming the next tile's K tiles
+ * through the ring while the consumers finish the current one.  The
+ * results are bit-identical to the per-tile kernel.  PGEMM_ERR_SHAPE for
+ * any other mode.  Not meant to be changed while other threads launch. */
+pgemm_status pgemm_set_persistent(int mode);
 
 /* Test hook for the credit protocol.  Sets, for later *_ws launches in this
  * process, the poll limit of every credit wait (0 restores the default) and

@@ -455,4 +455,106 @@ __global__ void __launch_bounds__(G::THREADS)
   }
 }
 
+// ============================================== NT, WS, persistent schedule
+
+// Persistent producer/consumer kernel (Croqtile ch.5, "persistent scheduling
+// and the if guard"): a fixed grid of at most one workgroup per CU, each
+// striding over output tiles tile_iter # block_id = tile_iter * gridDim.x +
+// blockIdx.x while that is below the tile count.  The producers stream one
+// continuous sequence of (tile, K tile) pairs through the ring, so the next
+// tile's loads overlap the last MMAs and the epilogue of the current one;
+// the credit counters keep counting across tiles (round of sequence entry g
+// = g / S).  Consumers store each finished tile straight from registers, as
+// the ring is already refilling.  Results are bit-identical to nt_ws_kernel
+// (same tiles, same k order per element).
+template <typename T, class G>
+__global__ void __launch_bounds__(G::THREADS)
+    nt_ws_persistent_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
+                            uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m,
+                            uint32_t max_polls, int skip_seed, uint32_t *err) {
+  static_assert(G::P > 0, "producer/consumer kernel needs producer waves");
+  using Loader = typename G::Loader;
+  using Row = RingRow<G::BK>;
+  constexpr int S = G::S, C = G::CW, P = G::P;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  uint32_t *full = reinterpret_cast<uint32_t *>(smem + G::CTR_OFFSET);
+  uint32_t *empty = full + S;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tiles = (int64_t)tiles_m * tiles_n;
+  const int n_k = K > 0 ? (K + G::BK - 1) / G::BK : 0;
+  // tiles tile_iter * gridDim.x + blockIdx.x below `tiles` (gridDim.x <= tiles)
+  const int my_tiles = (int)((tiles - 1 - blockIdx.x) / gridDim.x) + 1;
+  auto tile_of = [&](int it, int *bm, int *bn) {
+    int split;
+    block_work((int64_t)it * gridDim.x + blockIdx.x, tiles, tiles_m, tiles_n, group_m, bm, bn, &split);
+  };
+  auto slot_ptr = [&](int s) { return smem + s * Loader::SLOT_BYTES; };
+
+  if (tid < 2 * S) full[tid] = 0u;  // full[0..S) and empty[0..S)
+  __syncthreads();
+
+  if (wave < C) {
+    // ---------------------------------------------------------- consumer
+    WaveTile<T, G::WM, G::WN, G::BK> w;
+    const int wm = wave / G::WGN, wn = wave % G::WGN;
+    if (!skip_seed)
+      for (int s = 0; s < S; ++s) credit_trigger(&empty[s]);  // every slot starts free
+    uint32_t g = 0;  // position in the workgroup's (tile, K tile) sequence
+    for (int it = 0; it < my_tiles; ++it) {
+      int bm, bn;
+      tile_of(it, &bm, &bn);
+      w.zero();
+      for (int t = 0; t < n_k; ++t, ++g) {
+        const int s = (int)(g % S);
+        credit_wait(&full[s], (uint32_t)P * (g / S + 1u), max_polls, err);
+        char *base = slot_ptr(s);
+        w.template mma_ktile<false>(base + wm * G::WM * Row::ROW_BYTES,
+                                    base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
+        wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
+        credit_trigger(&empty[s]);
+      }
+      w.store_direct(out, M, N, bm * G::BM + wm * G::WM, bn * G::BN + wn * G::WN, lane);
+    }
+  } else {
+    // ---------------------------------------------------------- producer
+    // As in nt_ws_kernel: loads direct to LDS once the slot's `empty` credit
+    // arrives, `full` of sequence entry g triggered LAG = S - 2 entries
+    // later, now across tile boundaries.
+    constexpr int PER = G::PER_LOADER;
+    constexpr int LAG = S >= 2 ? S - 2 : 0;
+    static_assert((LAG + 1) * PER < 64, "loads in flight fit the 6-bit vmcnt");
+    const int first = (wave - C) * PER;
+    Loader ld;
+    uint32_t g = 0;
+    for (int it = 0; it < my_tiles; ++it) {
+      int bm, bn;
+      tile_of(it, &bm, &bn);
+      ld.init(lhs, rhs, M, N, K, 0, K, bm * G::BM, bn * G::BN);
+      for (int t = 0; t < n_k; ++t, ++g) {
+        const int s = (int)(g % S);
+        credit_wait(&empty[s], (uint32_t)C * (g / S + 1u), max_polls, err);
+        ld.template load<PER>(slot_ptr(s), t, first, lane);
+        if (g >= (uint32_t)LAG) {
+          wait_vmcnt<LAG * PER>();  // entry g - LAG landed
+          credit_trigger(&full[(g - LAG) % S]);
+        }
+      }
+    }
+    if constexpr (LAG >= 2) {
+      if (g >= 2) {
+        wait_vmcnt<PER>();
+        credit_trigger(&full[(g - 2) % S]);
+      }
+    }
+    if constexpr (LAG >= 1) {
+      if (g >= 1) {
+        wait_vmcnt<0>();
+        credit_trigger(&full[(g - 1) % S]);
+      }
+    }
+  }
+}
+
 }  // namespace pgemm

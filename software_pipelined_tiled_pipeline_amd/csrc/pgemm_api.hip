@@ -50,6 +50,15 @@ constexpr int kPieceAlign = 64;       // the small tile's K tile
 
 std::atomic<int> g_force_tile{0};
 std::atomic<int> g_force_split{0};
+std::atomic<int> g_persist_mode{0};  // 0 planned, 1 never, 2 always (producer/consumer calls)
+
+// Persistent producer/consumer schedule: a grid of at most kCUs x (workgroups
+// that fit a CU's LDS, at most 2) workgroups striding over the tiles.  The
+// planner does not choose it: with tiles of equal size it removes neither
+// the last wave's quantisation nor more than the per-tile fill and epilogue,
+// and it measured no faster than the per-tile kernel at 4096^3 and 8192^3.
+// pgemm_set_persistent(2) selects it.
+constexpr int64_t kCUs = 256;  // compute units of an MI355X
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -57,6 +66,7 @@ struct Plan {
   int tile = 0;         // 256 or 128 (NT calls), 16 (int32 call)
   int stages = 0;
   int split = 1;        // K pieces
+  bool persistent = false;
   int64_t k_chunk = 0;  // K elements per piece (K itself without a split)
   int64_t ldp = 0;      // row pitch of the partial-sum planes, in floats
   pgemm_kernel_info info{};
@@ -96,6 +106,11 @@ void fill_nt(Plan *p, int64_t M, int64_t N) {
   i->grid = cdiv(M, G::BM) * cdiv(N, G::BN) * p->split;
   i->k_tiles = cdiv(p->k_chunk, G::BK);
   i->k_split = p->split;
+  if (p->persistent) {
+    const int64_t per_cu = std::min<int64_t>(2, kLdsLimit / G::LDS_BYTES);
+    i->grid = std::min<int64_t>(i->grid, kCUs * per_cu);
+    i->persistent = 1;
+  }
   i->workspace_bytes = p->split > 1 ? p->split * M * p->ldp * (int64_t)sizeof(float) : 0;
 }
 
@@ -171,6 +186,7 @@ pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, Plan
       if (s < 1 || s > (ws ? kWsMaxStages : kSwapMaxStages)) return PGEMM_ERR_STAGES;
       p->stages = s;
       choose_tiling(p, M, N, K);
+      if (ws && p->split == 1) p->persistent = g_persist_mode.load(std::memory_order_relaxed) == 2;
       bool ok;
       if (p->tile == kLargeTile)
         ok = ws ? fill_nt_s<WsGeom>(p, s, M, N) : fill_nt_s<SwapGeom>(p, s, M, N);
@@ -326,6 +342,31 @@ pgemm_status launch_nt(const NtArgs &a, const Plan &p, float *part) {
   return launched();
 }
 
+template <typename T, class G>
+pgemm_status launch_ws_persistent(const NtArgs &a, const Plan &p) {
+  static std::atomic<uint64_t> lds_set{0};
+  auto kern = nt_ws_persistent_kernel<T, G>;
+  pgemm_status st = allow_lds(kern, G::LDS_BYTES, a.dev, lds_set);
+  if (st != PGEMM_OK) return st;
+  const int tm = (int)cdiv(a.M, G::BM), tn = (int)cdiv(a.N, G::BN);
+  const uint32_t polls = g_max_polls.load(std::memory_order_relaxed);
+  const int skip = g_skip_seed.load(std::memory_order_relaxed);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.info.grid), dim3(G::THREADS), G::LDS_BYTES, a.stream, a.lhs, a.rhs, a.out,
+                     a.M, a.N, a.K, tm, tn, kGroupM, polls, skip, g_err_ptr[a.dev]);
+  return launched();
+}
+
+template <typename T, template <int> class Geo>
+pgemm_status launch_ws_persistent_s(const NtArgs &a, const Plan &p) {
+  switch (p.stages) {
+    case 1: return launch_ws_persistent<T, Geo<1>>(a, p);
+    case 2: return launch_ws_persistent<T, Geo<2>>(a, p);
+    case 3: return launch_ws_persistent<T, Geo<3>>(a, p);
+    case 4: return launch_ws_persistent<T, Geo<4>>(a, p);
+  }
+  return PGEMM_ERR_STAGES;
+}
+
 template <typename T, template <int> class Geo, bool SPLIT, bool WS>
 pgemm_status launch_nt_s(const NtArgs &a, const Plan &p, float *part) {
   switch (p.stages) {
@@ -351,6 +392,8 @@ pgemm_status nt_entry(pgemm_op op, const uint16_t *lhs, const uint16_t *rhs, uin
   st = current_device(&a.dev);
   if (st != PGEMM_OK) return st;
   const bool ws = op == PGEMM_OP_NT_WS;
+  if (p.persistent)
+    return p.tile == kLargeTile ? launch_ws_persistent_s<T, WsGeom>(a, p) : launch_ws_persistent_s<T, WsGeomSmall>(a, p);
   if (p.tile == kLargeTile)
     return ws ? launch_nt_s<T, WsGeom, false, true>(a, p, nullptr)
               : launch_nt_s<T, SwapGeom, false, false>(a, p, nullptr);
@@ -461,6 +504,12 @@ pgemm_status pgemm_plan_arena(int32_t n, const pgemm_lds_block *blocks, int64_t 
   *arena_bytes = planner::pack(bl, &off);
   *no_reuse_bytes = sum;
   for (int32_t i = 0; i < n; ++i) offsets[i] = off[(size_t)i];
+  return PGEMM_OK;
+}
+
+pgemm_status pgemm_set_persistent(int mode) {
+  if (mode < 0 || mode > 2) return PGEMM_ERR_SHAPE;
+  g_persist_mode.store(mode, std::memory_order_relaxed);
   return PGEMM_OK;
 }
 

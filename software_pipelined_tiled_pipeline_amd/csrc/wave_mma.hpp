@@ -187,6 +187,55 @@ struct WaveTile {
     }
   }
 
+  // Rounds the accumulators to T and stores them straight to out[M][N] at
+  // (row0, col0), for kernels whose LDS ring is still in use when a tile
+  // ends.  Lane l (row l % 32) holds columns 8q + 4 (l / 32) .. +3 of each
+  // 32-column block; lanes l and l + 32 trade two of their four quads (one
+  // cross-lane exchange) so that each lane then owns two runs of eight
+  // consecutive columns and writes them as 16-byte stores.  Rows past M and
+  // columns past N are skipped.
+  __device__ __forceinline__ void store_direct(uint16_t *out, int M, int N, int row0, int col0, int lane) const {
+    const int r = lane & 31;
+    const int hi = lane >> 5;
+    const bool vec_ok = (N & 7) == 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = row0 + 32 * i + r;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const f32x16 &a = acc[i][j];
+        u32x2 p[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p[q] = Mfma<T>::pack4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+        // lane hi=0 keeps quads 0, 2 and sends 1, 3; lane hi=1 the reverse
+        const u32x2 s0 = hi ? p[0] : p[1], s1 = hi ? p[2] : p[3];
+        u32x2 r0, r1;
+        r0[0] = (uint32_t)__shfl_xor((int)s0[0], 32);
+        r0[1] = (uint32_t)__shfl_xor((int)s0[1], 32);
+        r1[0] = (uint32_t)__shfl_xor((int)s1[0], 32);
+        r1[1] = (uint32_t)__shfl_xor((int)s1[1], 32);
+        // hi=0: columns 0-7 (own quad 0, partner's quad 0) and 16-23;
+        // hi=1: columns 8-15 (partner's quad 1, own quad 1) and 24-31
+        const u32x4 c0 = hi ? u32x4{r0[0], r0[1], p[1][0], p[1][1]} : u32x4{p[0][0], p[0][1], r0[0], r0[1]};
+        const u32x4 c1 = hi ? u32x4{r1[0], r1[1], p[3][0], p[3][1]} : u32x4{p[2][0], p[2][1], r1[0], r1[1]};
+        if (row >= M) continue;
+        uint16_t *rp = out + (int64_t)row * N;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 v = h ? c1 : c0;
+          const int col = col0 + 32 * j + 16 * h + 8 * hi;
+          if (vec_ok && col + 8 <= N) {
+            *reinterpret_cast<u32x4 *>(rp + col) = v;
+          } else {
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+              if (col + x < N) rp[col + x] = (uint16_t)(v[x / 2] >> (16 * (x % 2)));
+          }
+        }
+      }
+    }
+  }
+
   // Rounds the accumulators to T and writes them into an LDS staging tile
   // (row pitch `pitch` bytes) at this wave's (row0, col0).
   __device__ __forceinline__ void stage(char *st, int pitch, int row0, int col0, int lane) const {

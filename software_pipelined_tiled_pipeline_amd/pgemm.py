@@ -33,7 +33,7 @@ class KernelInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "block_m", "block_n", "block_k", "stages", "producer_waves", "consumer_waves", "threads", "lds_bytes")] + [
         ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("k_split", ctypes.c_int32),
-        ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
+        ("persistent", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
 
 
 _lib = None
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.pgemm_sync_status.restype = I
         L.pgemm_set_tiling.argtypes = [I, I]
         L.pgemm_set_tiling.restype = I
+        L.pgemm_set_persistent.argtypes = [I]
+        L.pgemm_set_persistent.restype = I
         L.pgemm_set_ws_debug.argtypes = [I64, I]
         L.pgemm_set_ws_debug.restype = None
         L.pgemm_strerror.argtypes = [I]
@@ -148,6 +150,11 @@ def pgemm_sync_status(stream=None) -> int:
 def pgemm_set_tiling(tile: int = 0, k_split: int = 0) -> None:
     """Forces the tiling of later NT calls (0, 0 restores the planner)."""
     _check(lib().pgemm_set_tiling(int(tile), int(k_split)), "pgemm_set_tiling")
+
+
+def pgemm_set_persistent(mode: int = 0) -> None:
+    """Producer/consumer schedule of later calls: 0 planned, 1 never, 2 always persistent."""
+    _check(lib().pgemm_set_persistent(int(mode)), "pgemm_set_persistent")
 
 
 def pgemm_set_ws_debug(max_polls: int = 0, skip_seed: bool = False) -> None:

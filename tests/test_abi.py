@@ -86,6 +86,7 @@ def test_planner_on_the_workloads(L, op):
     for n in (8192, 4096):
         q = pgemm.pgemm_query(op, 0, n, n, n)
         assert (q["block_m"], q["block_n"], q["k_split"]) == (256, 256, 1)
+        assert q["persistent"] == 0
         assert q["grid"] == (n // 256) ** 2 and q["workspace_bytes"] == 0
     # ragged bf16 4095 x 1000 x 1000: 64 large tiles, so small ones (256)
     q = pgemm.pgemm_query(op, 0, 4095, 1000, 1000)
@@ -122,6 +123,31 @@ def test_planner_invariants(L, M, N, K, force):
             assert q["lds_bytes"] <= 160 * 1024
     finally:
         pgemm.pgemm_set_tiling(0, 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 8192, 8192), (4096, 4096, 64), (300, 200, 1000), (2560, 2048, 136),
+                                   (128, 8192, 16384)])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_persistent_schedule_plan(L, M, N, K, mode):
+    pgemm.pgemm_set_persistent(mode)
+    try:
+        for S in (1, 2, 3, 4):
+            q = pgemm.pgemm_query("nt_ws", S, M, N, K)
+            tiles = cdiv(M, q["block_m"]) * cdiv(N, q["block_n"])
+            if q["k_split"] > 1:
+                assert q["persistent"] == 0  # split products keep the per-tile kernel
+                continue
+            expect = mode == 2
+            assert q["persistent"] == int(expect)
+            if expect:
+                per_cu = min(2, (160 * 1024) // q["lds_bytes"])
+                assert q["grid"] == min(tiles, 256 * per_cu)
+            else:
+                assert q["grid"] == tiles
+            assert pgemm.pgemm_query("nt_swap", S, M, N, K)["persistent"] == 0
+    finally:
+        pgemm.pgemm_set_persistent(0)
+    assert L.pgemm_set_persistent(3) == ERR_SHAPE and L.pgemm_set_persistent(-1) == ERR_SHAPE
 
 
 def test_set_tiling_rejects(L):

@@ -298,6 +298,80 @@ def test_split_workspace_per_stream_and_growth(pg):
         assert_within_bound("f16", results[i], ref, mag, f"split {split}")
 
 
+# --------------------------------------------------- persistent schedule
+
+@contextlib.contextmanager
+def persistence(pg, mode):
+    pg.pgemm_set_persistent(mode)
+    try:
+        yield
+    finally:
+        pg.pgemm_set_persistent(0)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("tile,M,N,K", [(128, 2560, 2048, 136), (128, 2600, 2050, 72), (256, 4608, 4352, 264),
+                                        (256, 4100, 4500, 8), (128, 300, 200, 64)])
+def test_persistent_matches_per_tile_kernel(pg, fmt, tile, M, N, K):
+    # more tiles than the persistent grid holds, so workgroups stride over
+    # several tiles (ragged edges in the last ones); same bits as the
+    # per-tile kernel, and inside the bound on sampled elements
+    kind = "f16_nt" if fmt == "f16" else "bf16_nt"
+    A, B = inputs.make_operands(kind, M, N, K, 31 + M + K)
+    dA, dB = dev_half(A, fmt), dev_half(B, fmt)
+    with tiling(pg, tile, 1):
+        for S in (1, 2, 3, 4):
+            with persistence(pg, 2):
+                q = pg.pgemm_query("nt_ws", S, M, N, K)
+                assert q["persistent"] == 1
+                got = run_nt(pg, fmt, "ws", A, B, S, dA, dB)
+            with persistence(pg, 1):
+                ref_bits = run_nt(pg, fmt, "ws", A, B, S, dA, dB)
+            assert np.array_equal(got, ref_bits), f"persistent S={S} differs from the per-tile kernel"
+    check_sampled(fmt, A, B, {"persistent": got}, 7, count=1024)
+    assert pg.pgemm_sync_status() == 0
+
+
+def test_persistent_k_zero(pg):
+    dA = torch.zeros((700, 0), dtype=torch.float16, device="cuda")
+    dB = torch.zeros((900, 0), dtype=torch.float16, device="cuda")
+    with tiling(pg, 128, 1), persistence(pg, 2):
+        out = pg.pgemm_f16_nt_ws(dA, dB, out=torch.full((700, 900), 3.0, dtype=torch.float16, device="cuda"))
+        torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+
+
+# ------------------------------------------------ concurrent streams
+
+def test_many_small_gemms_on_concurrent_streams(pg):
+    # independent products on four streams at once (Croqtile ch.5,
+    # parallel.async with a stream per grid): each call only enqueues, the
+    # grids may overlap on the device, and every result must be the one a
+    # lone call gives (the K-split ones use their stream's own workspace)
+    shapes = [(256, 384, 512), (300, 200, 1000), (128, 1024, 4096), (520, 260, 136), (64, 2048, 2048),
+              (1000, 130, 64), (128, 512, 8192), (384, 384, 384)]
+    cases = []
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = inputs.make_operands("f16_nt", M, N, K, 900 + i)
+        cases.append((A, B, dev_half(A, "f16"), dev_half(B, "f16")))
+    alone = []
+    for i, (A, B, dA, dB) in enumerate(cases):
+        alone.append(run_nt(pg, "f16", "ws" if i % 2 else "swap", A, B, 2 + i % 3, dA, dB))
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        for i, (A, B, dA, dB) in enumerate(cases):
+            f = pg.pgemm_f16_nt_ws if i % 2 else pg.pgemm_f16_nt
+            outs.append((i, f(dA, dB, stages=2 + i % 3, stream=streams[(i + rep) % 4])))
+    torch.cuda.synchronize()
+    for i, o in outs:
+        assert np.array_equal(host_bits(o), alone[i]), f"case {i} differs when run concurrently"
+    for i, (A, B, _, _) in enumerate(cases):
+        ref, mag = oracle.gemm_nt("f16", A, B)
+        assert_within_bound("f16", alone[i], ref, mag, f"case {i}")
+
+
 # ----------------------------------------------------- credit protocol
 
 def test_missing_seed_times_out_instead_of_hanging(pg):
@@ -318,3 +392,14 @@ def test_missing_seed_times_out_instead_of_hanging(pg):
     ref, mag = oracle.gemm_nt("f16", A, B)
     assert_within_bound("f16", got, ref, mag, "after reset")
     assert pg.pgemm_sync_status() == 0
+    # the persistent kernel's waits are bounded the same way
+    with tiling(pg, 128, 1), persistence(pg, 2):
+        try:
+            pg.pgemm_set_ws_debug(max_polls=2000, skip_seed=True)
+            pg.pgemm_f16_nt_ws(dA, dB, stages=2)
+            assert pg.pgemm_sync_status() == 7
+        finally:
+            pg.pgemm_set_ws_debug(0, False)
+        assert pg.pgemm_sync_status() == 0
+        got = run_nt(pg, "f16", "ws", A, B, 2, dA, dB)
+    assert_within_bound("f16", got, ref, mag, "persistent, after reset")
