@@ -1,6 +1,6 @@
 // Device-side building blocks shared by the pgemm kernels (gfx950 only).
 //
-//  * vector types for the v_mfma_f32_32x32x16_{f16,bf16} operands;
+//  * vector types for the v_mfma_f32_16x16x32_{f16,bf16} operands;
 //  * buffer resources and direct-to-LDS 16-byte loads
 //    (buffer_load_dwordx4 ... lds), whose out-of-range lanes read zero;
 //  * the LDS ring: S slots, each an A tile [BM][BK] followed by a B tile
@@ -16,7 +16,6 @@ namespace pgemm {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

@@ -231,7 +231,7 @@ struct NtGeom {
   static constexpr int CTR_OFFSET = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
   static constexpr int LDS_BYTES = CTR_OFFSET + (P > 0 ? 2 * S * 4 : 0);
   static_assert(Loader::INSTR % LOADERS == 0, "loads split evenly");
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave blocks are whole 32x32 MFMA tiles");
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave blocks are whole 16x16 MFMA tiles");
   static_assert(S <= 4, "vmcnt wait table covers three tiles in flight");
   static_assert(P > 0 || S * PER_LOADER < 64, "in-flight loads fit the 6-bit vmcnt");
 };
@@ -240,7 +240,7 @@ struct NtGeom {
 
 // Every wave fills its share of the ring with direct-to-LDS loads and runs
 // MFMA on its own block; one workgroup barrier per K tile.  The fragments of
-// k16 step kk+1 are read while step kk's MFMAs run (two fragment sets), and
+// k32 step kk+1 are read while step kk's MFMAs run (two fragment sets), and
 // the barrier sits at the start of a tile's last step rather than at the
 // tile boundary, so the stream of MFMAs does not stop at tiles:
 //
@@ -249,24 +249,32 @@ struct NtGeom {
 //       is complete once every wave has passed);
 //     - every read of tile t has been issued and drained (WAR: tile t's slot
 //       is free once every wave has passed);
-//   after it: loads of tile t+S into tile t's slot are issued, the first
-//   fragments of tile t+1 are read, and tile t's last MFMAs run.
+//   after it: all loads of tile t+S into tile t's slot are issued, spread
+//   over that step's MFMAs, while the first fragments of tile t+1 are read
+//   and tile t's last MFMAs run.
 //
 // The loads of a tile are issued S-1 tiles ahead (at the barrier in tile
-// t-S, when its slot comes free).  S = 1
-// has a single slot and runs fill -> barrier -> compute -> barrier.
+// t-S, when its slot comes free) and have S-1 tiles minus one step to land.
+// A tile of a single k32 step (BK = 32) has its barrier at the start of its
+// only step; the fragment sets then alternate per tile, so the loop body
+// covers two tiles.  S = 1 has a single slot and runs fill -> barrier ->
+// compute -> barrier.
 template <typename T, class G, bool SPLIT>
 __global__ void __launch_bounds__(G::THREADS, G::OCC)
     nt_swap_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
                    uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m,
                    int k_chunk, float *__restrict__ partial, int ldp) {
   static_assert(G::P == 0, "single-schedule kernel has no producer waves");
+  // Epilogue arguments are read into SGPRs up front: a scalar load still in
+  // flight when the main loop starts would turn the loop's first fragment
+  // wait into a wait for every outstanding LDS read.
+  __asm__ volatile("" ::"s"(out), "s"(partial), "s"(ldp));
   using Loader = typename G::Loader;
   using Row = RingRow<G::BK>;
   using W = WaveTile<T, G::WM, G::WN, G::BK>;
   constexpr int S = G::S;
-  constexpr int NK = G::BK / 16;
-  static_assert(NK % 2 == 0, "fragment sets alternate per step and must line up per tile");
+  constexpr int NK = W::NK;
+  static_assert(NK == 1 || NK % 2 == 0, "fragment sets alternate per step and line up per tile or tile pair");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -285,7 +293,7 @@ __global__ void __launch_bounds__(G::THREADS, G::OCC)
   w.zero();
   auto slot_ptr = [&](int s) { return smem + s * Loader::SLOT_BYTES; };
   const int first = wave * G::PER_LOADER;
-  const int r = lane & 31, hi = lane >> 5, sw = Row::swz(r);
+  const int r = W::lane_row(lane), chunk = W::lane_chunk(lane), sw = Row::swz(r);
   auto lane_a = [&](int s) { return slot_ptr(s) + (wm * G::WM + r) * Row::ROW_BYTES; };
   auto lane_b = [&](int s) { return slot_ptr(s) + (G::BM + wn * G::WN + r) * Row::ROW_BYTES; };
 
@@ -297,62 +305,68 @@ __global__ void __launch_bounds__(G::THREADS, G::OCC)
       lds_barrier();
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        W::read_frags(f, lane_a(0), lane_b(0), kk, hi, sw);
+        W::read_frags(f, lane_a(0), lane_b(0), kk, chunk, sw);
         w.mma_step(f);
       }
       lds_barrier();
     }
   } else {
-    // A slot freed at the barrier of tile t is refilled with tile t+S: half
-    // of this wave's loads during tile t's last step, half during the first
-    // step of tile t+1, each spread out between MFMAs (see mixed_step).  The
-    // prologue issues tiles 0 .. S-2 and the first half of tile S-1, so the
-    // steady state starts as if a refill were under way.  Loads of tiles at
-    // or past the end read only out-of-range offsets (zeros into slots no
-    // later tile uses); issuing them anyway keeps every vmcnt target static.
+    // The prologue issues tiles 0 .. S-1.  Loads of tiles at or past the
+    // end read only out-of-range offsets (zeros into slots no later tile
+    // uses); issuing them anyway keeps every vmcnt target static.
     constexpr int PER = G::PER_LOADER;
-    constexpr int HALF = PER / 2;
-    static_assert(PER % 2 == 0 && HALF % Loader::PAR == 0, "refill loads split in halves");
     typename W::Frags f[2];
     NoLoads no_load;
-    for (int j = 0; j + 1 < S; ++j) ld.template load<PER>(slot_ptr(j), j, first, lane);
-    ld.template load<HALF>(slot_ptr(S - 1), S - 1, first, lane);
-    wait_vmcnt<(S - 2) * PER + HALF>();  // tile 0 landed
+    for (int j = 0; j < S; ++j) ld.template load<PER>(slot_ptr(j), j, first, lane);
+    wait_vmcnt<(S - 1) * PER>();  // tile 0 landed
     lds_barrier();
-    if (n_k > 0) W::read_frags(f[0], lane_a(0), lane_b(0), 0, hi, sw);
-    int refill = S - 1, rslot = S - 1;
-    // steps 0 .. NK-2 of tile t (step 0 carries the second half of the refill)
-    auto head = [&](int t) __attribute__((always_inline)) {
-      const int s = t % S;
-      w.template mixed_step<true, HALF>(f[0], f[1], lane_a(s), lane_b(s), 1, hi, sw,
-                                        RefillLoads<Loader>{ld, slot_ptr(rslot), refill, first + HALF});
-#pragma unroll
-      for (int kk = 1; kk + 1 < NK; ++kk)
-        w.template mixed_step<true, 0>(f[kk & 1], f[(kk + 1) & 1], lane_a(s), lane_b(s), kk + 1, hi, sw, no_load);
-    };
-    // (the last tile is peeled off so that the loop body has one path)
-    for (int t = 0; t + 1 < n_k; ++t) {
-      const int s = t % S;
-      head(t);
-      // tile t+1 complete once every wave has waited for its own share;
-      // still in flight after it: tiles t+2 .. t+S-1
-      wait_vmcnt<(S - 2) * PER>();
+    if (n_k > 0) W::read_frags(f[0], lane_a(0), lane_b(0), 0, chunk, sw);
+    // Barrier of tile t, then its last step on f[C], which reads the first
+    // fragments of tile t+1 into f[C ^ 1] and refills tile t's slot with
+    // tile t+S.  Still in flight at the wait: tiles t+2 .. t+S-1.
+    auto last_step = [&](int t, auto cur) __attribute__((always_inline)) {
+      constexpr int C = decltype(cur)::value;
+      wait_vmcnt<(S - 2) * PER>();  // tile t+1 landed
       lds_barrier();
-      refill = t + S;  // into tile t's slot, now free
-      rslot = s;
       const int s1 = (t + 1) % S;
-      w.template mixed_step<true, HALF>(f[1], f[0], lane_a(s1), lane_b(s1), 0, hi, sw,
-                                        RefillLoads<Loader>{ld, slot_ptr(s), t + S, first});
-    }
-    if (n_k > 0) {
-      head(n_k - 1);
-      w.template mixed_step<false, 0>(f[1], f[0], lane_a(0), lane_b(0), 0, hi, sw, no_load);
+      w.template mixed_step<true, PER>(f[C], f[C ^ 1], lane_a(s1), lane_b(s1), 0, chunk, sw,
+                                       RefillLoads<Loader>{ld, slot_ptr(t % S), t + S, first});
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    if constexpr (NK == 1) {
+      // One step per tile, f[t & 1] holding tile t.  The last tile runs the
+      // same step as the others: its reads of the tile after it and its
+      // refill only touch slots that are not read again (the refill reads
+      // zeros), and one code path keeps the accumulators in place.
+      for (int t = 0; t < n_k; t += 2) {
+        last_step(t, C0{});
+        if (t + 1 < n_k) last_step(t + 1, C1{});
+      }
+    } else {
+      // steps 0 .. NK-2 of tile t; the last step then runs on f[1]
+      auto head = [&](int t) __attribute__((always_inline)) {
+        const int s = t % S;
+#pragma unroll
+        for (int kk = 0; kk + 1 < NK; ++kk)
+          w.template mixed_step<true, 0>(f[kk & 1], f[(kk + 1) & 1], lane_a(s), lane_b(s), kk + 1, chunk, sw,
+                                         no_load);
+      };
+      for (int t = 0; t + 1 < n_k; ++t) {
+        head(t);
+        last_step(t, C1{});
+      }
+      if (n_k > 0) {
+        head(n_k - 1);
+        w.template mixed_step<false, 0>(f[1], f[0], lane_a(0), lane_b(0), 0, chunk, sw, no_load);
+      }
     }
   }
   // Loads of tiles past the end are still in flight (they read zeros); none
   // may land after this point, where the ring becomes the staging tile or
   // the workgroup ends.
   wait_vmcnt<0>();
+  w.settle();
   if constexpr (SPLIT) {
     w.store_partial(partial + (int64_t)split * M * ldp, ldp, M, N, m0 + wm * G::WM, n0 + wn * G::WN, lane);
   } else {
@@ -392,7 +406,7 @@ __global__ void __launch_bounds__(G::THREADS)
   if (tid < 2 * S) full[tid] = 0u;  // full[0..S) and empty[0..S)
   __syncthreads();
 
-  WaveTile<T, G::WM, G::WN, G::BK> w;
+  WaveTile<T, G::WM, G::WN, G::BK, false> w;
   const int wm = wave / G::WGN, wn = wave % G::WGN;
   if (wave < C) {
     // ---------------------------------------------------------- consumer
@@ -404,11 +418,12 @@ __global__ void __launch_bounds__(G::THREADS)
       const uint32_t round = (uint32_t)(t / S);
       credit_wait(&full[s], (uint32_t)P * (round + 1u), max_polls, err);
       char *base = slot_ptr(s);
-      w.template mma_ktile<false>(base + wm * G::WM * Row::ROW_BYTES,
-                                  base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
+      w.template mma_ktile<1>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES,
+                              lane);
       wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
       credit_trigger(&empty[s]);
     }
+    w.settle();
   } else {
     // ---------------------------------------------------------- producer
     Loader ld;
@@ -497,7 +512,7 @@ __global__ void __launch_bounds__(G::THREADS)
 
   if (wave < C) {
     // ---------------------------------------------------------- consumer
-    WaveTile<T, G::WM, G::WN, G::BK> w;
+    WaveTile<T, G::WM, G::WN, G::BK, false> w;
     const int wm = wave / G::WGN, wn = wave % G::WGN;
     if (!skip_seed)
       for (int s = 0; s < S; ++s) credit_trigger(&empty[s]);  // every slot starts free
@@ -510,11 +525,11 @@ __global__ void __launch_bounds__(G::THREADS)
         const int s = (int)(g % S);
         credit_wait(&full[s], (uint32_t)P * (g / S + 1u), max_polls, err);
         char *base = slot_ptr(s);
-        w.template mma_ktile<false>(base + wm * G::WM * Row::ROW_BYTES,
-                                    base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
+        w.template mma_ktile<0>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
         wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
         credit_trigger(&empty[s]);
       }
+      w.settle();
       w.store_direct(out, M, N, bm * G::BM + wm * G::WM, bn * G::BN + wn * G::WN, lane);
     }
   } else {

@@ -1,19 +1,27 @@
 // Consumer-side math and the output epilogue.
 //
-// A wave owns a WM x WN block of the output, held as (WM/32) x (WN/32) fp32
-// accumulators of v_mfma_f32_32x32x16.  Operand roles: src0 is the rhs
-// fragment (32 rows n) and src1 the lhs fragment (32 rows m), so each
-// accumulator holds a transposed 32x32 output block:
-//   lane l, register r of acc[i][j] ->
-//     out[m0 + 32 i + l % 32][n0 + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4],
-// i.e. registers 4q..4q+3 are four consecutive columns of one row, which the
-// epilogue writes as one 8-byte piece.
+// A wave owns a WM x WN block of the output, held as (WM/16) x (WN/16) fp32
+// accumulators of v_mfma_f32_16x16x32.  Operand roles: src0 is the rhs
+// fragment (16 rows n) and src1 the lhs fragment (16 rows m), so each
+// accumulator holds a transposed 16x16 output block:
+//   lane l, register r of acc[i][j] -> out[m0 + 16 i + l % 16][n0 + 16 j + 4 (l / 16) + r],
+// i.e. a lane's four registers are four consecutive columns of one row.
 //
 // Both fragments are read the same way from a ring slot: lane l reads row
-// (base + l % 32) at chunk 2 kk + l / 32 (eight consecutive k), for the k16
-// step kk of the tile.  Every output element accumulates the k16 steps in
+// (base + l % 16) at chunk 4 kk + l / 16 (eight consecutive k), for the k32
+// step kk of the tile.  Every output element accumulates the k32 steps in
 // increasing k, so any tile shape, stage count or variant gives the same
 // bits.
+//
+// On gfx950 this shape sustains the same MFMA rate per clock as 32x32x16 and
+// draws less power per flop (a quarter of the accumulator traffic per
+// instruction), which matters on a chip whose clock is set by its power
+// limit.  The MFMAs are written as inline asm with the accumulator tied to
+// the destination: with the builtin, a loop body that updates each of 64
+// small accumulators more than once is register-allocated with copies
+// between AGPRs and VGPRs.  The compiler's hazard tracking does not look
+// inside asm statements, so the wait states an MFMA result needs before
+// other instructions read it are inserted by hand (settle(), zero()).
 #pragma once
 
 #include "device_common.hpp"
@@ -25,9 +33,13 @@ struct Mfma;
 
 template <>
 struct Mfma<_Float16> {
-  __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  // acc += src0 x src1^T over 32 k; ACC_AGPR picks the register file of acc
+  template <bool ACC_AGPR>
+  __device__ __forceinline__ static void run(u32x4 src0, u32x4 src1, f32x4 &acc) {
+    if constexpr (ACC_AGPR)
+      asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(src0), "v"(src1));
+    else
+      asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(src0), "v"(src1));
   }
   // fp32 -> binary16, round to nearest even (v_cvt_f16_f32 in the default mode)
   __device__ __forceinline__ static u32x2 pack4(float a, float b, float c, float d) {
@@ -39,9 +51,12 @@ struct Mfma<_Float16> {
 
 template <>
 struct Mfma<__bf16> {
-  __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  template <bool ACC_AGPR>
+  __device__ __forceinline__ static void run(u32x4 src0, u32x4 src1, f32x4 &acc) {
+    if constexpr (ACC_AGPR)
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(src0), "v"(src1));
+    else
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(src0), "v"(src1));
   }
   // fp32 -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32)
   __device__ __forceinline__ static u32x2 pack4(float a, float b, float c, float d) {
@@ -51,109 +66,146 @@ struct Mfma<__bf16> {
   }
 };
 
-template <typename T, int WM, int WN, int BK>
+// ACC_AGPR: accumulators in AGPRs (one wave per SIMD, 256 of them) or in
+// VGPRs (kernels with several waves per SIMD and a smaller block).
+template <typename T, int WM, int WN, int BK, bool ACC_AGPR = true>
 struct WaveTile {
-  static constexpr int TM = WM / 32;
-  static constexpr int TN = WN / 32;
+  static constexpr int TM = WM / 16;
+  static constexpr int TN = WN / 16;
+  static constexpr int NK = BK / 32;  // k32 steps per K tile
+  static_assert(WM % 16 == 0 && WN % 16 == 0 && BK % 32 == 0, "whole 16x16x32 MFMA tiles");
   using Row = RingRow<BK>;
-  f32x16 acc[TM][TN];
+  f32x4 acc[TM][TN];
 
+  // lane -> row within a 16-row block / 16-byte chunk within a k32 step
+  __device__ __forceinline__ static int lane_row(int lane) { return lane & 15; }
+  __device__ __forceinline__ static int lane_chunk(int lane) { return lane >> 4; }
+
+  // Ties every accumulator to its register at this point of the program:
+  // accumulator reads and writes cannot move across it or across the
+  // volatile asm statements around it.
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (ACC_AGPR)
+          asm volatile("" : "+a"(acc[i][j]));
+        else
+          asm volatile("" : "+v"(acc[i][j]));
+      }
+  }
+
+  // Zeroes the accumulators, with the wait states a register written by a
+  // VALU instruction needs before an MFMA reads it as srcC.
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+    pin();
+    asm volatile("s_nop 4");
   }
 
-  // Fragments of one k16 step: TN rhs and TM lhs 16-byte pieces per lane.
+  // Wait states between the last MFMA and any other instruction that reads
+  // or overwrites its accumulator (24; an 8-pass MFMA result needs 11).
+  __device__ __forceinline__ void settle() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    pin();
+  }
+
+  // Fragments of one k32 step: TN rhs and TM lhs 16-byte pieces per lane.
   struct Frags {
     u32x4 b[TN], a[TM];
   };
 
-  // Lane l reads row (base + l % 32) at chunk 2 kk + l / 32 of the K tile;
-  // `lane_a` / `lane_b` already point at that row of the wave's first block.
   // `lane_a` / `lane_b` point at the lane's row of the wave's first lhs /
-  // rhs block in a slot; s = swz(l % 32).
+  // rhs block in a slot (blocks are 16 rows apart); chunk = lane_chunk(l),
+  // s = swz(lane_row(l)), the same for every block since blocks start at
+  // multiples of 16 rows.
   __device__ __forceinline__ static void read_frags(Frags &f, const char *lane_a, const char *lane_b, int kk,
-                                                    int hi, int s) {
-    const int p = ((2 * kk + hi) ^ s) * 16;
+                                                    int chunk, int s) {
+    const int p = ((4 * kk + chunk) ^ s) * 16;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const u32x4 *>(lane_b + 32 * j * Row::ROW_BYTES + p);
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const u32x4 *>(lane_b + 16 * j * Row::ROW_BYTES + p);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const u32x4 *>(lane_a + 32 * i * Row::ROW_BYTES + p);
+    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const u32x4 *>(lane_a + 16 * i * Row::ROW_BYTES + p);
   }
 
   __device__ __forceinline__ void mma_step(const Frags &f) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T>::run(f.b[j], f.a[i], acc[i][j]);
+      for (int j = 0; j < TN; ++j) Mfma<T>::template run<ACC_AGPR>(f.b[j], f.a[i], acc[i][j]);
   }
 
-  // One K tile from a ring slot.  a_rows / b_rows: LDS address of the first
-  // of this wave's lhs / rhs rows in the slot; both are multiples of 32 rows
-  // from the tile start, so the swizzle term depends on l % 32 only.  With
-  // PREFETCH the fragments of step kk+1 are read while step kk's MFMAs run
-  // (two fragment sets live); without it one set is live and latency is left
-  // to the other waves of the SIMD.
-  template <bool PREFETCH>
+  // One K tile from a ring slot with a single fragment set: the rhs pieces
+  // of a k32 step first, then the lhs pieces, AHEAD (0 or 1) block rows
+  // before the MFMAs that use them.  a_rows / b_rows: LDS address of the
+  // first of this wave's lhs / rhs rows in the slot.
+  template <int AHEAD>
   __device__ __forceinline__ void mma_ktile(const char *a_rows, const char *b_rows, int lane) {
-    const int r = lane & 31;
-    const int hi = lane >> 5;
+    static_assert(AHEAD == 0 || AHEAD == 1, "at most one lhs piece read ahead");
+    const int r = lane_row(lane);
+    const int chunk = lane_chunk(lane);
     const int s = Row::swz(r);
     const char *lane_a = a_rows + r * Row::ROW_BYTES;
     const char *lane_b = b_rows + r * Row::ROW_BYTES;
-    constexpr int NK = BK / 16;
-    if constexpr (PREFETCH) {
-      Frags f[2];
-      read_frags(f[0], lane_a, lane_b, 0, hi, s);
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        if (kk + 1 < NK) read_frags(f[(kk + 1) & 1], lane_a, lane_b, kk + 1, hi, s);
-        mma_step(f[kk & 1]);
-      }
-    } else {
+    for (int kk = 0; kk < NK; ++kk) {
+      const int p = ((4 * kk + chunk) ^ s) * 16;
+      u32x4 b[TN], a[2];
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        Frags f;
-        read_frags(f, lane_a, lane_b, kk, hi, s);
-        mma_step(f);
+      for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const u32x4 *>(lane_b + 16 * j * Row::ROW_BYTES + p);
+      if constexpr (AHEAD) a[0] = *reinterpret_cast<const u32x4 *>(lane_a + p);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (AHEAD) {
+          if (i + 1 < TM)
+            a[(i + 1) & 1] = *reinterpret_cast<const u32x4 *>(lane_a + 16 * (i + 1) * Row::ROW_BYTES + p);
+        } else {
+          a[i & 1] = *reinterpret_cast<const u32x4 *>(lane_a + 16 * i * Row::ROW_BYTES + p);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) Mfma<T>::template run<ACC_AGPR>(b[j], a[i & 1], acc[i][j]);
       }
     }
   }
 
-  // One k16 step: the TM*TN MFMAs on `cf`, with, in a fixed interleave
-  // (one read every TM*TN/(TM+TN) MFMAs, one load every TM*TN/NLOAD), the
-  // fragment reads of the next step into `nf` when READS and NLOAD calls
-  // ld_fn(0 .. NLOAD-1).  sched_barrier(0) after every MFMA pins the order:
-  // global loads spaced out between MFMAs never pile up in the
-  // texture-address queue, where a full queue would stall the wave's
+  // One k32 step: the TM*TN MFMAs on `cf`, interleaved in a fixed order
+  // with (when READS) the TM+TN fragment reads of the next step into `nf`,
+  // one every RE MFMAs over the first half of the step, and NLOAD calls
+  // ld_fn(0 .. NLOAD-1), one every TM*TN/NLOAD MFMAs.  Reads finish early so
+  // that the wait before a barrier or before the next step finds them done;
+  // loads are spread over the whole step.  sched_barrier(0) after every
+  // MFMA pins the order: global loads spaced out between MFMAs never pile up
+  // in the texture-address queue, where a full queue would stall the wave's
   // in-order issue, MFMAs included.
   template <bool READS, int NLOAD, class LoadFn>
   __device__ __forceinline__ void mixed_step(const Frags &cf, Frags &nf, const char *lane_a, const char *lane_b,
-                                             int nkk, int hi, int s, LoadFn &&ld_fn) {
+                                             int nkk, int chunk, int s, LoadFn &&ld_fn) {
     constexpr int NM = TM * TN;
     constexpr int NR = TM + TN;
-    static_assert(NM % NR == 0 || !READS, "reads spread evenly");
+    constexpr int RE = NM / NR / 2 > 0 ? NM / NR / 2 : 1;  // MFMAs per read
+    static_assert(!READS || NR * RE <= NM, "reads fit in the step");
     static_assert(NLOAD == 0 || NM % NLOAD == 0, "loads spread evenly");
-    constexpr int RE = NM / NR;                         // MFMAs per read
     constexpr int LE = NLOAD > 0 ? NM / (NLOAD > 0 ? NLOAD : 1) : NM + 1;  // MFMAs per load
-    const int p = ((2 * nkk + hi) ^ s) * 16;
+    const int p = ((4 * nkk + chunk) ^ s) * 16;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int m = i * TN + j;
-        acc[i][j] = Mfma<T>::run(cf.b[j], cf.a[i], acc[i][j]);
+        Mfma<T>::template run<ACC_AGPR>(cf.b[j], cf.a[i], acc[i][j]);
         if constexpr (READS) {
-          if (m % RE == RE - 1) {
+          if (m % RE == RE - 1 && m / RE < NR) {
             const int r = m / RE;
             if (r < TN)
-              nf.b[r] = *reinterpret_cast<const u32x4 *>(lane_b + 32 * r * Row::ROW_BYTES + p);
+              nf.b[r] = *reinterpret_cast<const u32x4 *>(lane_b + 16 * r * Row::ROW_BYTES + p);
             else
-              nf.a[r - TN] = *reinterpret_cast<const u32x4 *>(lane_a + 32 * (r - TN) * Row::ROW_BYTES + p);
+              nf.a[r - TN] = *reinterpret_cast<const u32x4 *>(lane_a + 16 * (r - TN) * Row::ROW_BYTES + p);
           }
         }
         if constexpr (NLOAD > 0) {
@@ -165,93 +217,81 @@ struct WaveTile {
 
   // Writes the fp32 accumulators, unrounded, to a row-major partial-sum
   // matrix (row pitch ldp floats, a multiple of 4) at (row0, col0); rows
-  // past M and column groups past N are skipped.  Each lane stores 16 bytes
-  // (four consecutive columns) per register quad.
+  // past M and column groups past N are skipped.  Each lane stores its four
+  // consecutive columns as one 16-byte piece.  Call settle() first.
   __device__ __forceinline__ void store_partial(float *base, int ldp, int M, int N, int row0, int col0,
                                                 int lane) const {
-    const int r = lane & 31;
-    const int hi = lane >> 5;
+    const int r = lane_row(lane);
+    const int g = lane_chunk(lane);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int row = row0 + 32 * i + r;
+      const int row = row0 + 16 * i + r;
       if (row >= M) continue;
       float *rp = base + (int64_t)row * ldp;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = col0 + 32 * j + 8 * q + 4 * hi;
-          const f32x16 &a = acc[i][j];
-          if (col < N) *reinterpret_cast<f32x4 *>(rp + col) = f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-        }
+      for (int j = 0; j < TN; ++j) {
+        const int col = col0 + 16 * j + 4 * g;
+        if (col < N) *reinterpret_cast<f32x4 *>(rp + col) = acc[i][j];
+      }
     }
   }
 
   // Rounds the accumulators to T and stores them straight to out[M][N] at
   // (row0, col0), for kernels whose LDS ring is still in use when a tile
-  // ends.  Lane l (row l % 32) holds columns 8q + 4 (l / 32) .. +3 of each
-  // 32-column block; lanes l and l + 32 trade two of their four quads (one
-  // cross-lane exchange) so that each lane then owns two runs of eight
-  // consecutive columns and writes them as 16-byte stores.  Rows past M and
-  // columns past N are skipped.
+  // ends.  Lanes with chunk g and g^1 hold columns 4g..4g+3 of one row in
+  // blocks j and j+1; they trade one quad (one cross-lane exchange) so that
+  // each owns eight consecutive columns, of block j for even g and of block
+  // j+1 for odd g, and writes them as one 16-byte store.  Rows past M and
+  // columns past N are skipped.  Call settle() first.
   __device__ __forceinline__ void store_direct(uint16_t *out, int M, int N, int row0, int col0, int lane) const {
-    const int r = lane & 31;
-    const int hi = lane >> 5;
+    static_assert(TN % 2 == 0, "column blocks are paired");
+    const int r = lane_row(lane);
+    const int g = lane_chunk(lane);
+    const int odd = g & 1;
     const bool vec_ok = (N & 7) == 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int row = row0 + 32 * i + r;
+      const int row = row0 + 16 * i + r;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const f32x16 &a = acc[i][j];
-        u32x2 p[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) p[q] = Mfma<T>::pack4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
-        // lane hi=0 keeps quads 0, 2 and sends 1, 3; lane hi=1 the reverse
-        const u32x2 s0 = hi ? p[0] : p[1], s1 = hi ? p[2] : p[3];
-        u32x2 r0, r1;
-        r0[0] = (uint32_t)__shfl_xor((int)s0[0], 32);
-        r0[1] = (uint32_t)__shfl_xor((int)s0[1], 32);
-        r1[0] = (uint32_t)__shfl_xor((int)s1[0], 32);
-        r1[1] = (uint32_t)__shfl_xor((int)s1[1], 32);
-        // hi=0: columns 0-7 (own quad 0, partner's quad 0) and 16-23;
-        // hi=1: columns 8-15 (partner's quad 1, own quad 1) and 24-31
-        const u32x4 c0 = hi ? u32x4{r0[0], r0[1], p[1][0], p[1][1]} : u32x4{p[0][0], p[0][1], r0[0], r0[1]};
-        const u32x4 c1 = hi ? u32x4{r1[0], r1[1], p[3][0], p[3][1]} : u32x4{p[2][0], p[2][1], r1[0], r1[1]};
+      for (int j = 0; j < TN; j += 2) {
+        const f32x4 &a0 = acc[i][j];
+        const f32x4 &a1 = acc[i][j + 1];
+        const u32x2 p0 = Mfma<T>::pack4(a0[0], a0[1], a0[2], a0[3]);
+        const u32x2 p1 = Mfma<T>::pack4(a1[0], a1[1], a1[2], a1[3]);
+        const u32x2 snd = odd ? p0 : p1;
+        u32x2 rcv;
+        rcv[0] = (uint32_t)__shfl_xor((int)snd[0], 16);
+        rcv[1] = (uint32_t)__shfl_xor((int)snd[1], 16);
+        const u32x4 v = odd ? u32x4{rcv[0], rcv[1], p1[0], p1[1]} : u32x4{p0[0], p0[1], rcv[0], rcv[1]};
         if (row >= M) continue;
         uint16_t *rp = out + (int64_t)row * N;
+        const int col = col0 + 16 * (j + odd) + 8 * (g >> 1);
+        if (vec_ok && col + 8 <= N) {
+          *reinterpret_cast<u32x4 *>(rp + col) = v;
+        } else {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const u32x4 v = h ? c1 : c0;
-          const int col = col0 + 32 * j + 16 * h + 8 * hi;
-          if (vec_ok && col + 8 <= N) {
-            *reinterpret_cast<u32x4 *>(rp + col) = v;
-          } else {
-#pragma unroll
-            for (int x = 0; x < 8; ++x)
-              if (col + x < N) rp[col + x] = (uint16_t)(v[x / 2] >> (16 * (x % 2)));
-          }
+          for (int x = 0; x < 8; ++x)
+            if (col + x < N) rp[col + x] = (uint16_t)(v[x / 2] >> (16 * (x % 2)));
         }
       }
     }
   }
 
   // Rounds the accumulators to T and writes them into an LDS staging tile
-  // (row pitch `pitch` bytes) at this wave's (row0, col0).
+  // (row pitch `pitch` bytes) at this wave's (row0, col0), one 8-byte piece
+  // per block.  Call settle() first.
   __device__ __forceinline__ void stage(char *st, int pitch, int row0, int col0, int lane) const {
-    const int r = lane & 31;
-    const int hi = lane >> 5;
+    const int r = lane_row(lane);
+    const int g = lane_chunk(lane);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x16 &a = acc[i][j];
-          u32x2 v = Mfma<T>::pack4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
-          char *dst = st + (row0 + 32 * i + r) * pitch + (col0 + 32 * j + 8 * q + 4 * hi) * 2;
-          *reinterpret_cast<u32x2 *>(dst) = v;
-        }
+      for (int j = 0; j < TN; ++j) {
+        const f32x4 &a = acc[i][j];
+        const u32x2 v = Mfma<T>::pack4(a[0], a[1], a[2], a[3]);
+        char *dst = st + (row0 + 16 * i + r) * pitch + (col0 + 16 * j + 4 * g) * 2;
+        *reinterpret_cast<u32x2 *>(dst) = v;
+      }
   }
 };
 

@@ -121,11 +121,9 @@ def swap_programs(S: int, n_k: int, W: int, *, skip_barrier: bool = False, skip_
 
     Each wave's share of a tile is two halves (shares 2w and 2w + 1), issued
     as asynchronous loads that land later.  S = 1: load, wait, barrier, read,
-    barrier.  S >= 2: the prologue issues tiles 0 .. S-2 and the first half
-    of tile S-1; the head of tile t issues the second half of the refill
-    chosen at the previous barrier (tile S-1 before the loop) and reads tile
-    t; then the wave waits for its own loads of tile t+1, meets the others at
-    the barrier, and issues the first half of tile t+S into tile t's slot.
+    barrier.  S >= 2: the prologue issues tiles 0 .. S-1; the wave reads
+    tile t, waits for its own loads of tile t+1, meets the others at the
+    barrier and then issues both halves of tile t+S into tile t's slot.
     Loads of tiles at or past n_k are issued too (they read zeros in the
     kernel); before the epilogue the wave waits for all of its loads.
 
@@ -149,28 +147,25 @@ def swap_programs(S: int, n_k: int, W: int, *, skip_barrier: bool = False, skip_
                     prog.append((BARRIER, nb)); nb += 1
             progs.append(prog)
             continue
-        for j in range(S - 1):
+        for j in range(S):
             prog += [(ISSUE, j % S, j, a), (ISSUE, j % S, j, b)]
-        prog.append((ISSUE, (S - 1) % S, S - 1, a))
         if not skip_wait:
             prog.append((WAITLOADS, 0))
         if not skip_barrier:
             prog.append((BARRIER, nb)); nb += 1
-        refill = S - 1
         for t in range(n_k):
             s = t % S
-            prog.append((ISSUE, refill % S, refill, b))  # second half of the pending refill
             prog += [(RBEGIN, s, t), (REND, s, t)]
             if t + 1 < n_k:
+                refill = [(ISSUE, (t + S) % S, t + S, a), (ISSUE, (t + S) % S, t + S, b)]
                 if refill_before_barrier:
-                    prog.append((ISSUE, (t + S) % S, t + S, a))
+                    prog += refill
                 if not skip_wait:
                     prog.append((WAITLOADS, t + 1))
                 if not skip_barrier:
                     prog.append((BARRIER, nb)); nb += 1
                 if not refill_before_barrier:
-                    prog.append((ISSUE, (t + S) % S, t + S, a))
-                refill = t + S
+                    prog += refill
         prog.append((WAITLOADS, 10 ** 9))  # the epilogue waits for every load
         progs.append(prog)
     return progs, 2 * W

@@ -10,9 +10,13 @@ consumer for `full`; Croqtile ch.5, bootstrap protocol: without the initial
 done lets the producer overwrite a slot in use), and the kernels' own wait
 constants, checked against the model's wait points.
 """
+import os
+
 import pytest
 
 from protocol_model import ISSUE, WAITLOADS, check_swap, check_ws, swap_programs
+
+KERNELS = os.path.join(os.path.dirname(__file__), "..", "software_pipelined_tiled_pipeline_amd", "csrc", "kernels.hpp")
 
 
 # ------------------------------------------------------ correct schedules
@@ -52,11 +56,11 @@ def test_ws_protocol_safe_on_random_interleavings(S, n_k, P, C):
 
 def test_kernel_wait_constants_match_the_model():
     # nt_swap_kernel waits with s_waitcnt vmcnt(N) for static N: (S-2)*PER
-    # before each barrier and (S-2)*PER + PER/2 in the prologue, PER loads
-    # per wave and tile issued in two halves.  In the model one ISSUE is one
-    # half, so at each wait for "tiles <= u landed" exactly 2(S-2) issues
-    # (2(S-2) + 1 in the prologue) of later tiles may still be in flight, and
-    # every issue of a tile <= u comes before them (loads complete in order).
+    # before each barrier and (S-1)*PER in the prologue, PER loads per wave
+    # and tile.  In the model one ISSUE is half of them, so at each wait for
+    # "tiles <= u landed" exactly 2(S-2) issues (2(S-1) in the prologue) of
+    # later tiles may still be in flight, and every issue of a tile <= u
+    # comes before them (loads complete in order).
     for S in (2, 3, 4):
         for n_k in (1, 2, 5, 9):
             prog = swap_programs(S, n_k, 1)[0][0]
@@ -66,10 +70,13 @@ def test_kernel_wait_constants_match_the_model():
                 u = prog[i][1]
                 issues = [ins for ins in prog[:i] if ins[0] == ISSUE]
                 later = [ins for ins in issues if ins[2] > u]
-                expect = 2 * (S - 2) + (1 if j == 0 else 0)
+                expect = 2 * (S - 1) if j == 0 else 2 * (S - 2)
                 assert len(later) == expect, (S, n_k, u)
                 first_later = next((k for k, ins in enumerate(issues) if ins[2] > u), len(issues))
                 assert all(ins[2] > u for ins in issues[first_later:])
+    src = open(KERNELS).read()
+    assert "wait_vmcnt<(S - 1) * PER>();  // tile 0 landed" in src
+    assert "wait_vmcnt<(S - 2) * PER>();  // tile t+1 landed" in src
 
 
 # ------------------------------------------------------ planted mistakes
