@@ -129,6 +129,14 @@ __device__ __forceinline__ uint32_t credit_peek(const uint32_t *ctr) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// The counter's value as an ordinary LDS load: the compiler places the wait
+// for it before its first use, so it can be issued well ahead of that.  For
+// waves that issue no direct-to-LDS loads (those would make the compiler wait
+// for them before any LDS read it cannot prove disjoint).
+__device__ __forceinline__ uint32_t credit_load(const uint32_t *ctr) {
+  return __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 __device__ __forceinline__ void credit_trigger(uint32_t *ctr) {
   if ((threadIdx.x & (kWave - 1)) == 0)
     asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(ctr)), "v"(1u) : "memory");

@@ -413,15 +413,22 @@ __global__ void __launch_bounds__(G::THREADS)
     if (!skip_seed)
       for (int s = 0; s < S; ++s) credit_trigger(&empty[s]);  // every slot starts free
     w.zero();
+    // `full` of the next tile's slot is read at the start of each tile and
+    // checked after its MFMAs, so a credit that has already arrived costs no
+    // LDS round trip; only a short one is waited for.
+    uint32_t seen = 0;
     for (int t = 0; t < n_k; ++t) {
       const int s = t % S;
-      const uint32_t round = (uint32_t)(t / S);
-      credit_wait(&full[s], (uint32_t)P * (round + 1u), max_polls, err);
+      const uint32_t target = (uint32_t)P * ((uint32_t)(t / S) + 1u);
+      if (seen < target) credit_wait(&full[s], target, max_polls, err);
+      compiler_fence();
+      const uint32_t next = t + 1 < n_k ? credit_load(&full[(t + 1) % S]) : 0u;
       char *base = slot_ptr(s);
       w.template mma_ktile<1>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES,
                               lane);
       wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
       credit_trigger(&empty[s]);
+      seen = __builtin_amdgcn_readfirstlane(next);
     }
     w.settle();
   } else {
@@ -525,7 +532,8 @@ __global__ void __launch_bounds__(G::THREADS)
         const int s = (int)(g % S);
         credit_wait(&full[s], (uint32_t)P * (g / S + 1u), max_polls, err);
         char *base = slot_ptr(s);
-        w.template mma_ktile<0>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
+        w.template mma_ktile<0>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES,
+                                lane);
         wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
         credit_trigger(&empty[s]);
       }
