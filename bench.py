@@ -9,8 +9,9 @@ finds fastest; the single-schedule kernel is swept too and reported beside it.
 
 Prints one JSON line (rank 0) with TFLOP/s, the roofline position of the
 kernel (average launch time from HIP events on the launch stream) beside the
-MFMA-only rate the chip sustains under its power limit (libpgemm_probe.so),
-and the CPU oracle timed on a bounded sample of the same product.  Other
+rate of an MFMA-only loop of the same instruction (libpgemm_probe.so; a
+reference point for the power-limited clock, not an upper bound), and the CPU
+oracle timed on a bounded sample of the same product.  Other
 workloads (--workload): 4096^3, the ragged bf16 4095 x 1000 x 1000 and the
 skinny 128 x 8192 x 16384 product (reported against the HBM roofline).
 """
@@ -80,7 +81,7 @@ def time_launches(fn, reps, stream):
     return e0.elapsed_time(e1) / reps
 
 
-def mfma_ceiling():
+def mfma_only_loop():
     """MFMA-only rate and shader clock from libpgemm_probe.so (no memory
     traffic), on random and on zero operands; None if the probe fails."""
     import ctypes
@@ -285,12 +286,12 @@ def main():
         },
     }
     if args.workload != "f16_nt_skinny":
-        ceiling = mfma_ceiling()
-        if ceiling:
-            # what the chip sustains under its power limit with no memory
-            # traffic at all: context for `frac`, whose peak is the nominal one
-            ceiling["frac_of_random_operand_ceiling"] = round(achieved / ceiling["random_operands"]["tflops"], 4)
-            result["roofline"]["mfma_only_ceiling"] = ceiling
+        loop = mfma_only_loop()
+        if loop:
+            # the GEMM's MFMA with no memory traffic, at the clock the power
+            # limit allows: context for `frac`, whose peak is the nominal one
+            loop["frac_of_random_operand_loop"] = round(achieved / loop["random_operands"]["tflops"], 4)
+            result["roofline"]["mfma_only_loop"] = loop
     if args.workload == "f16_nt_skinny":
         alg_bytes = (M * K + N * K + M * N) * 2
         result["roofline"].update({

@@ -64,18 +64,19 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // A ring slot holds the A tile (rows of lhs) and then the B tile (rows of
 // rhs), both K-contiguous.  A row of BK halves is CPR = BK/8 granules of 16
 // bytes.  Logical chunk c of row r is stored at position c ^ swz(r), where
-// swz(r) = (r / (16 / CPR)) mod CPR.  With that choice any 16 consecutive
-// rows read at the same chunk touch 16 different granules of a 256-byte
-// window, so the fragment reads (lane l reads row base + l%32) are free of
-// bank conflicts; the direct-to-LDS writes fill 1 KiB contiguously per
-// instruction and never conflict.
+// swz(r) = (r / 2) mod CPR.  The fragment reads of a 16x16x32 MFMA (lane l
+// reads row base + l % 16 at chunk 4 kk + l / 16, base a multiple of 16)
+// then run at the LDS read rate of a linear access for both row widths;
+// the previous swizzle, (r / (16 / CPR)) mod CPR, which suits lanes reading
+// 32 rows at one chunk, ran the 64-byte rows at two thirds of that (measured
+// with ds_read_b128 on gfx950).  The direct-to-LDS writes fill 1 KiB
+// contiguously per instruction and never conflict.
 template <int BK>
 struct RingRow {
   static constexpr int CPR = BK / 8;              // granules per row
   static constexpr int ROW_BYTES = BK * 2;
-  static constexpr int ROWS_PER_WINDOW = 16 / CPR; // rows per 256 bytes
   static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
-  __device__ __forceinline__ static int swz(int r) { return (r / ROWS_PER_WINDOW) % CPR; }
+  __device__ __forceinline__ static int swz(int r) { return (r >> 1) % CPR; }
 };
 
 // Work of a workgroup: output tile (bm, bn) and K piece `split`.

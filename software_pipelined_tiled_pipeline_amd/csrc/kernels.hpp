@@ -103,9 +103,11 @@ struct SlotLoader {
   static constexpr int SLOT_BYTES = (BM + BN) * Row::ROW_BYTES;
   static constexpr int RPI = kWave / CPR;  // rows per instruction
   // Within instruction jj (of the A or the B tile), lane l covers row
-  // jj * RPI + l / CPR; its swizzle is (4 jj + l / 16) mod CPR, so the lane's
-  // chunk depends on jj only through jj mod PAR.
+  // jj * RPI + l / CPR, whose swizzle ((jj * RPI + l / CPR) / 2) mod CPR
+  // depends on jj only through jj mod PAR (RPI / 2 = 32 / CPR is a multiple
+  // of CPR / PAR).
   static constexpr int PAR = CPR / 4;
+  static_assert((RPI / 2) * PAR % CPR == 0, "swizzle period in instructions");
   static_assert(A_INSTR % PAR == 0, "instruction parity is the same in both tiles");
   static_assert((BM * CPR) % kWave == 0 && (BN * CPR) % kWave == 0, "tiles fill whole instructions");
 
@@ -134,7 +136,7 @@ struct SlotLoader {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int p = 0; p < PAR; ++p) {
-      const int chunk = (lane % CPR) ^ ((4 * p + lane / 16) % CPR);
+      const int chunk = (lane % CPR) ^ Row::swz(p * RPI + lane / CPR);
       lane_off[p] = (uint32_t)(lane / CPR) * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
       lane_k[p] = chunk * 8;
     }

@@ -1,10 +1,13 @@
-// Measurement aid, not part of the GEMM path: the rate v_mfma_f32_32x32x16_f16
-// sustains on this device with no memory traffic at all, and the shader
-// clock it runs at.  Every wave keeps 16 accumulator tiles and two sets of
-// operand fragments and alternates between the sets, so the operand bits
-// change every 16 MFMAs as they do in a GEMM.  With random operands the rate
-// is bounded by the chip's power limit rather than by MFMA issue; with zero
-// operands it shows the issue-bound rate.
+// Measurement aid, not part of the GEMM path: the rate v_mfma_f32_16x16x32_f16
+// (the GEMM's instruction) sustains on this device with no memory traffic at
+// all, and the shader clock it runs at.  Every wave keeps the GEMM's 8 x 8
+// accumulator tiles (in AGPRs, tied to the instruction as in the GEMM) and
+// two sets of operand fragments, and alternates between the sets, so the
+// operand bits change every 64 MFMAs as they do in a GEMM.  With random
+// operands the chip runs it at the clock its power limit allows; with zero
+// operands it shows the issue-bound rate.  A GEMM also spends power on data
+// movement and loses issue slots to it, so this loop is a reference point,
+// not an upper bound that a GEMM could not pass.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -13,10 +16,10 @@
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGrid = 1024, kThreads = 256;
+constexpr int kGrid = 1024, kThreads = 256, kBlocks = 8;
 
 // binary16 bits of a value uniform in [-1, 1): SplitMix64 of the index
 // (Steele, Lea & Flood 2014), top 53 bits as a fraction, rounded by the
@@ -33,40 +36,50 @@ __device__ uint32_t operand_bits(uint64_t i) {
 
 __device__ u32x4 fragment(int zero, uint64_t base) {
   u32x4 v;
+#pragma unroll
   for (int k = 0; k < 4; ++k)
     v[k] = zero ? 0u : (operand_bits(base + 2 * k) | (operand_bits(base + 2 * k + 1) << 16));
   return v;
 }
 
-__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
-                                                0);
+__device__ __forceinline__ void mfma(u32x4 a, u32x4 b, f32x4 &c) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
 __global__ void __launch_bounds__(kThreads, 1) mfma_loop(int zero, int iters, float *sink, uint64_t *clocks) {
   const uint64_t lane = threadIdx.x & 63;
-  u32x4 a[2][4], b[2][4];
+  u32x4 a[2][kBlocks], b[2][kBlocks];
+#pragma unroll
   for (int s = 0; s < 2; ++s)
-    for (int r = 0; r < 4; ++r) {
-      a[s][r] = fragment(zero, ((uint64_t)(s * 8 + r) * 64 + lane) * 8);
-      b[s][r] = fragment(zero, ((uint64_t)(s * 8 + 4 + r) * 64 + lane) * 8);
+#pragma unroll
+    for (int r = 0; r < kBlocks; ++r) {
+      a[s][r] = fragment(zero, ((uint64_t)(s * 2 * kBlocks + r) * 64 + lane) * 8);
+      b[s][r] = fragment(zero, ((uint64_t)(s * 2 * kBlocks + kBlocks + r) * 64 + lane) * 8);
     }
-  f32x16 acc[4][4];
+  f32x4 acc[kBlocks][kBlocks];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kBlocks; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kBlocks; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+      asm volatile("" : "+a"(acc[i][j]));
+    }
+  asm volatile("s_nop 4");  // accumulator writes -> MFMA srcC
   const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kBlocks; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma(b[s][j], a[s][i], acc[i][j]);
+        for (int j = 0; j < kBlocks; ++j) mfma(b[s][j], a[s][i], acc[i][j]);
   }
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // last MFMA -> reads of its result
+#pragma unroll
+  for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j) asm volatile("" : "+a"(acc[i][j]));
   const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     clocks[0] = t1 - t0;  // shader clock cycles
@@ -74,11 +87,11 @@ __global__ void __launch_bounds__(kThreads, 1) mfma_loop(int zero, int iters, fl
   }
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kBlocks; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kBlocks; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s += acc[i][j][r];
+      for (int r = 0; r < 4; ++r) s += acc[i][j][r];
   sink[blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
@@ -101,8 +114,8 @@ extern "C" int pgemm_probe_mfma(int zero_operands, int64_t iters, double *tflops
   if (hipEventRecord(e1, nullptr) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) goto done;
   if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess || ms <= 0.0f) goto done;
   if (hipMemcpy(c, clocks, sizeof c, hipMemcpyDeviceToHost) != hipSuccess || c[1] == 0) goto done;
-  // 4 waves x iters x 32 MFMAs x 32x32x16x2 flop per workgroup
-  *tflops = (double)kGrid * 4 * (double)iters * 32 * 32768.0 / (ms * 1e-3) / 1e12;
+  // 4 waves x iters x 2 sets x 64 MFMAs x 16x16x32x2 flop per workgroup
+  *tflops = (double)kGrid * 4 * (double)iters * 2 * kBlocks * kBlocks * 16384.0 / (ms * 1e-3) / 1e12;
   *sclk_ghz = (double)c[0] / ((double)c[1] * 10.0);
   rc = 0;
 done:
