@@ -6,7 +6,7 @@ type, with ref and sum_k |a*b| from the binary64 oracle.  Small shapes are
 compared in full; the full-size workloads are compared on sampled elements
 (the oracle computes each one alone) plus whole edge rows and columns, and
 across stages, variants and tile sizes for bit identity (every kernel
-accumulates the k16 MFMA steps of an element in the same order; only a K
+accumulates the k32 MFMA steps of an element in the same order; only a K
 split changes the order, into per-piece sums added in piece order).
 """
 import contextlib
@@ -92,7 +92,10 @@ def test_s32_ragged_and_wrapping(pg, M, N, K, stages):
 
 # ------------------------------------------------- NT, full comparisons
 
-SMALL = [(520, 300, 200), (257, 129, 136), (64, 64, 8), (1, 1, 8), (300, 1000, 64), (513, 257, 1000)]
+# K from one K tile up: at BK = 32 these give 7, 5, 1, 1, 2, 32, 3 and 4 K tiles
+# (odd and even counts for the single schedule's two-tile loop body)
+SMALL = [(520, 300, 200), (257, 129, 136), (64, 64, 8), (1, 1, 8), (300, 1000, 64), (513, 257, 1000), (96, 96, 96),
+         (130, 70, 128)]
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
