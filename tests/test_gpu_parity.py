@@ -125,6 +125,32 @@ def test_nt_small_all_variants(pg, fmt, M, N, K):
                 assert np.array_equal(first, unsplit), f"tile {tile} differs in bits from tile 256"
 
 
+def _random_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(count):
+        M = int(rng.integers(1, 521))
+        N = int(rng.integers(1, 521))
+        K = 8 * int(rng.integers(1, 129))  # rows of lhs/rhs start on 16 bytes
+        shapes.append((M, N, K))
+    return shapes
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", _random_shapes(2024, 6))
+def test_nt_random_shapes_planned(pg, fmt, M, N, K):
+    # seeded random shapes under the planner's own choice of tile and K
+    # split (small shapes here take 128x128 tiles and often a split)
+    kind = "f16_nt" if fmt == "f16" else "bf16_nt"
+    A, B = inputs.make_operands(kind, M, N, K, 7000 + M + 3 * N + 5 * K)
+    ref, mag = oracle.gemm_nt(fmt, A, B)
+    dA, dB = dev_half(A, fmt), dev_half(B, fmt)
+    q = pg.pgemm_query("nt_ws", 0, M, N, K)
+    for variant, s in [("swap", 2), ("swap", 4), ("ws", 3)]:
+        got = run_nt(pg, fmt, variant, A, B, s, dA, dB)
+        assert_within_bound(fmt, got, ref, mag, f"{fmt} {variant} S={s} {M}x{N}x{K} pieces {q['k_split']}")
+
+
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("tile,split", TILINGS)
 def test_nt_k_zero_gives_zeros(pg, fmt, tile, split):
