@@ -8,7 +8,8 @@ generator.  A step is one GEMM call of the producer/consumer kernel
 finds fastest; the single-schedule kernel is swept too and reported beside it.
 
 Prints one JSON line (rank 0) with TFLOP/s, the roofline position of the
-kernel (average launch time from HIP events on the launch stream) beside the
+kernel (average launch time from HIP events on the launch stream), the
+vendor library's rate on the same f16 operands (torch.matmul), the
 rate of an MFMA-only loop of the same instruction (libpgemm_probe.so; a
 reference point for the power-limited clock, not an upper bound), and the CPU
 oracle timed on a bounded sample of the same product.  Other
@@ -214,6 +215,17 @@ def main():
             ms = time_launches(call, 10, stream)
             sweep[f"{variant} S={s}"] = round(flops / (ms * 1e-3) / 1e12, 1)
             log(f"[bench] sweep {variant} S={s}: {ms * 1e3:.1f} us, {sweep[f'{variant} S={s}']} TFLOP/s")
+    # the vendor library on the same operands and stream, for context (f16
+    # only): torch.matmul with the K-contiguous rhs as a transposed view
+    reference = None
+    if fmt == "f16":
+        def ref_call():
+            t, a_, b_ = operands()
+            torch.matmul(a_, b_.t(), out=out)
+        time_launches(ref_call, 3, stream)
+        ms = time_launches(ref_call, 10, stream)
+        reference = {"call": "torch.matmul (hipBLASLt)", "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        log(f"[bench] torch.matmul: {ms * 1e3:.1f} us, {reference['tflops']} TFLOP/s")
     stages = args.stages
     if stages == 0:
         cands = {k: v for k, v in sweep.items() if k.startswith(args.variant + " ")}
@@ -285,6 +297,9 @@ def main():
             "kernel_avg_us": round(kern_ms * 1e3, 2),
         },
     }
+    if reference:
+        reference["ours_over_reference"] = round(achieved / reference["tflops"], 3)
+        result["reference_library"] = reference
     if args.workload != "f16_nt_skinny":
         loop = mfma_only_loop()
         if loop:
