@@ -8,6 +8,11 @@
 //                 one workgroup barrier per tile.
 //  nt_ws_kernel   f16/bf16 NT, producer waves and consumer waves coordinated
 //                 by per-slot full/empty credit counters in LDS.
+//  nt_ws_persistent_kernel
+//                 the same roles over a fixed grid that strides through the
+//                 output tiles, the ring and its credits running across them.
+//
+// The f16/bf16 kernels multiply with v_mfma_f32_16x16x32 (wave_mma.hpp).
 //
 // Pipelining follows Croqtile ch.6 ("Synchronization: pipelines, events and
 // double buffering") and the modulo schedule of the TileLang chapter
