@@ -211,8 +211,10 @@ def main():
     for variant, stage_set in (("ws", (1, 2, 3, 4)), ("swap", (1, 2, 3, 4))):
         for s in stage_set:
             call = launcher(variant, s)
-            time_launches(call, 3, stream)
-            ms = time_launches(call, 10, stream)
+            # at least ten launches and about 4 ms of them, so that short
+            # products are ranked on more than a few tens of microseconds
+            est = time_launches(call, 3, stream)
+            ms = time_launches(call, max(10, int(4.0 / max(est, 1e-3))), stream)
             sweep[f"{variant} S={s}"] = round(flops / (ms * 1e-3) / 1e12, 1)
             log(f"[bench] sweep {variant} S={s}: {ms * 1e3:.1f} us, {sweep[f'{variant} S={s}']} TFLOP/s")
     stages = args.stages
@@ -240,18 +242,22 @@ def main():
 
     # the vendor library on the same operands and stream, for context (f16
     # only): torch.matmul with the K-contiguous rhs as a transposed view,
-    # timed after our own timed region in three alternating rounds of ten
-    # launches of each, medians reported, so that neither side gets a
-    # clock state the other does not
+    # timed after our own timed region in three alternating rounds, medians
+    # reported.  In each round either side first runs untimed for about two
+    # milliseconds: ten launches of a 0.1 ms product right after the other
+    # side's ran measurably slower (the clock settles to each kernel's power
+    # draw in about a millisecond).
     reference = None
     if fmt == "f16":
         def ref_call():
             t, a_, b_ = operands()
             torch.matmul(a_, b_.t(), out=out)
-        time_launches(ref_call, 3, stream)
+        settle = max(3, int(2.0 / max(kern_ms, 1e-3)))
         ref_ms, ours_ms = [], []
         for _ in range(3):
+            time_launches(ref_call, settle, stream)
             ref_ms.append(time_launches(ref_call, 10, stream))
+            time_launches(step, settle, stream)
             ours_ms.append(time_launches(step, 10, stream))
         ms_ref, ms_ours = float(np.median(ref_ms)), float(np.median(ours_ms))
         reference = {"call": "torch.matmul (hipBLASLt)", "tflops": round(flops / (ms_ref * 1e-3) / 1e12, 1),
