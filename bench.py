@@ -14,7 +14,8 @@ rate of an MFMA-only loop of the same instruction (libpgemm_probe.so; a
 reference point for the power-limited clock, not an upper bound), and the CPU
 oracle timed on a bounded sample of the same product.  Other
 workloads (--workload): 4096^3, the ragged bf16 4095 x 1000 x 1000 and the
-skinny 128 x 8192 x 16384 product (reported against the HBM roofline).
+skinny 128 x 8192 x 16384 product (reported against the HBM roofline), and
+the int32 NN 128 x 256 x 256 product (GOP/s, single-schedule kernel).
 """
 from __future__ import annotations
 
@@ -31,9 +32,15 @@ sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2516.6   # 256 CUs x 4096 flop/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
+# int32 VALU: 4 SIMDs x 16 lanes per CU retire one full-rate instruction per
+# lane per clock; counting one multiply-add (2 ops) per lane-slot gives
+# 256 CUs x 64 x 2 x 2.4 GHz.  An upper bound for the int32 kernel, whose
+# 32-bit multiply issues below the full rate.
+PEAK_S32_TOPS = 256 * 64 * 2 * 2.4e9 / 1e12
 
 WORKLOADS = {
     # name: (M, N, K, seed workload index, element type)
+    "s32_nn_128x256x256": (128, 256, 256, 1, "s32"),
     "f16_nt_8192": (8192, 8192, 8192, 3, "f16"),
     "f16_nt_4096": (4096, 4096, 4096, 2, "f16"),
     "bf16_nt_ragged": (4095, 1000, 1000, 4, "bf16"),
@@ -121,6 +128,112 @@ def cpu_baseline(fmt, A, B, M, N, K, budget_s: float):
     }
 
 
+def run_s32(args, torch, np):
+    """The int32 NN product: GOP/s of back-to-back launches, the per-launch
+    duration distribution (median, min, p90 of 200 single launches), a
+    bit-exact check of the whole output against the oracle, and the oracle
+    timed on the whole product."""
+    import ctypes
+    from software_pipelined_tiled_pipeline_amd import inputs, pgemm
+
+    M, N, K, widx, _ = WORKLOADS[args.workload]
+    log(f"[bench] generating {args.workload} operands {M}x{N}x{K}")
+    A, B = inputs.make_operands("s32_nn", M, N, K, inputs.workload_seed(widx))
+    dev = torch.device("cuda:0")
+    dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    out = torch.empty((M, N), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    ops = 2.0 * M * N * K
+    f = pgemm.lib().pgemm_s32_nn
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    pa, pb, po = (ctypes.c_void_p(t.data_ptr()) for t in (dA, dB, out))
+
+    def launcher(s):
+        def call():
+            st = f(pa, pb, po, M, N, K, s, sptr)
+            if st != 0:
+                raise pgemm.PgemmError(st, "pgemm_s32_nn")
+        return call
+
+    time_launches(launcher(2), 200, stream)
+    sweep = {}
+    for s in (1, 2):
+        call = launcher(s)
+        time_launches(call, 20, stream)
+        ms = time_launches(call, 200, stream)
+        sweep[f"swap S={s}"] = round(ops / (ms * 1e-3) / 1e9, 1)
+        log(f"[bench] sweep swap S={s}: {ms * 1e3:.2f} us, {sweep[f'swap S={s}']} GOP/s")
+    stages = args.stages or int(max(sweep, key=sweep.get).split("S=")[1])
+    step = launcher(stages)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps of swap S={stages}")
+    t0 = time.perf_counter()
+    kern_ms = time_launches(step, args.steps, stream)
+    wall = time.perf_counter() - t0
+    single = sorted(time_launches(step, 1, stream) for _ in range(200))
+    value = ops * args.steps / wall / 1e9
+    achieved = ops / (kern_ms * 1e-3) / 1e12
+
+    import oracle
+    ref = oracle.gemm_s32_nn(A, B)
+    got = out.cpu().numpy()
+    bad = int(np.count_nonzero(got != ref))
+    if bad:
+        raise RuntimeError(f"timed output differs from the oracle in {bad} elements")
+
+    result = {
+        "metric": f"GOP/s for s32 NN GEMM {M}x{N}x{K}, 1 MI355X",
+        "value": round(value, 1),
+        "unit": "GOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"s32 NN GEMM M={M} N={N} K={K}, operands integers -8..8, wrapping int32 "
+                        "accumulation, single-schedule swap",
+            "M": M, "N": N, "K": K,
+            "variant": "swap",
+            "stages": stages,
+            "stage_sweep_gops": sweep,
+            "single_launch_us": {"median": round(single[100] * 1e3, 2), "min": round(single[0] * 1e3, 2),
+                                 "p90": round(single[180] * 1e3, 2), "launches": 200},
+            "parity": {"elements": M * N, "mismatches": bad},
+        },
+        "roofline": {
+            "bound": "alu",
+            "achieved": round(achieved, 4),
+            "peak": round(PEAK_S32_TOPS, 1),
+            "unit": "TOP/s",
+            "frac": round(achieved / PEAK_S32_TOPS, 5),
+            "traffic": None,
+            "kernel": "s32_nn_kernel",
+            "kernel_avg_us": round(kern_ms * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on the whole product")
+        reps, t = 1, 0.0
+        while True:
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                oracle.gemm_s32_nn(A, B)
+            t = time.perf_counter() - t0
+            if t > min(2.0, args.cpu_budget) or reps >= 1 << 16:
+                break
+            reps *= 4
+        result["cpu_baseline"] = {"value": ops * reps / t / 1e9, "unit": "GOP/s", "cores": oracle.threads(),
+                                  "kind": "oracle", "sample": f"the whole product, {reps} times, {t:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +272,9 @@ def main():
     from software_pipelined_tiled_pipeline_amd import inputs, pgemm
 
     pgemm.lib()  # fails loudly if the HIP library is missing
+    if WORKLOADS[args.workload][4] == "s32":
+        run_s32(args, torch, np)
+        return
     M, N, K, widx, fmt = WORKLOADS[args.workload]
     kind, tdt = ("f16_nt", torch.float16) if fmt == "f16" else ("bf16_nt", torch.bfloat16)
     log(f"[bench] generating {args.workload} operands {M}x{N}x{K}")

@@ -3,9 +3,10 @@
 //  s32_nn_kernel  int32 NN, one output per thread, VALU multiply-add,
 //                 prologue / steady / epilogue over a two-slot ring whose
 //                 slot roles are swapped after every tile.
-//  nt_swap_kernel f16/bf16 NT, one schedule for all waves: every wave issues
-//                 direct-to-LDS loads for tile t+S-1 and runs MFMA on tile t,
-//                 one workgroup barrier per tile.
+//  nt_swap_kernel f16/bf16 NT, one schedule for all waves: every wave runs
+//                 MFMA on tile t and, in tile t's last k32 step, refills
+//                 tile t's slot with its share of tile t+S (direct-to-LDS
+//                 loads); one workgroup barrier per tile.
 //  nt_ws_kernel   f16/bf16 NT, producer waves and consumer waves coordinated
 //                 by per-slot full/empty credit counters in LDS.
 //  nt_ws_persistent_kernel
