@@ -355,6 +355,12 @@ def main():
         raise RuntimeError("a credit wait gave up during the timed region")
     value = flops * args.steps / wall / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
+    # single launches, each between its own pair of events (they include the
+    # event overhead and a launch from idle): median, min and p90
+    n_single = 200 if kern_ms < 0.05 else 20
+    single = sorted(time_launches(step, 1, stream) for _ in range(n_single))
+    single_us = {"median": round(single[n_single // 2] * 1e3, 2), "min": round(single[0] * 1e3, 2),
+                 "p90": round(single[(9 * n_single) // 10] * 1e3, 2), "launches": n_single}
 
     # the vendor library on the same operands and stream, for context (f16
     # only): torch.matmul with the K-contiguous rhs as a transposed view,
@@ -417,6 +423,7 @@ def main():
             "stages": stages,
             "pct_of_mfma_peak": round(100.0 * value / PEAK_F16_TFLOPS, 1),
             "stage_sweep_tflops": sweep,
+            "single_launch_us": single_us,
             "parity": {"sampled": 256, "violations": bad, "worst_err_over_bound": round(worst, 4)},
         },
         "roofline": {

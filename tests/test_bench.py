@@ -56,6 +56,8 @@ def test_ragged_workload_line():
     assert COMMON <= set(j) and "cpu_baseline" not in j
     assert j["unit"] == "TFLOP/s" and j["dtype"] == "bf16" and j["config"]["variant"] == "ws"
     assert j["config"]["parity"]["violations"] == 0
+    lat = j["config"]["single_launch_us"]
+    assert lat["launches"] == 200 and 0 < lat["min"] <= lat["median"] <= lat["p90"]
     assert set(j["config"]["stage_sweep_tflops"]) == {f"{v} S={s}" for v in ("ws", "swap") for s in (1, 2, 3, 4)}
     roof = j["roofline"]
     assert roof["bound"] == "mfma" and 0 < roof["frac"] < 1 and roof["kernel"] == "nt_ws_kernel"
