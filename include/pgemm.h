@@ -41,7 +41,8 @@ extern "C" {
 typedef enum {
   PGEMM_OK = 0,
   PGEMM_ERR_NULL = 1,    /* a required pointer is NULL                       */
-  PGEMM_ERR_SHAPE = 2,   /* negative or too large M, N, K; bad tiling request */
+  PGEMM_ERR_SHAPE = 2,   /* negative or too large M, N, K; bad tiling request;
+                            an NT grid of 2^32 or more work-items            */
   PGEMM_ERR_STAGES = 3,  /* stages outside the set the entry point supports  */
   PGEMM_ERR_ALIGN = 4,   /* a pointer is not 16-byte aligned                 */
   PGEMM_ERR_LDS = 5,     /* the tile ring for these stages exceeds LDS       */
@@ -67,6 +68,8 @@ typedef enum {
  *   Sums wrap modulo 2^32 (two's complement).  Results are exact.
  *   Each workgroup is 16 x 16 threads owning a 16 x 16 output tile; K is
  *   cut into tiles of 16.  stages: 1 (one buffer, serial) or 2 (default).
+ *   The grid has one workgroup per output tile up to 2^20 workgroups; a
+ *   larger output is walked by that many, each taking every 2^20-th tile.
  */
 pgemm_status pgemm_s32_nn(const int32_t *lhs, const int32_t *rhs, int32_t *out,
                           int64_t M, int64_t N, int64_t K, int stages, void *stream);

@@ -30,64 +30,74 @@ namespace pgemm {
 
 // ================================================================ int32 NN
 
-// Thread (qx, qy) of workgroup (px, py) owns out[16 px + qx][16 py + qy];
+// Output tile (px, py) is out[16 px .. 16 px + 15][16 py .. 16 py + 15], and
+// thread (qx, qy) of the workgroup owns element (16 px + qx, 16 py + qy);
 // tile t of lhs is rows 16 px.., columns 16 t..; tile t of rhs is rows
 // 16 t.., columns 16 py...  Elements outside the matrices load as zero.
+// The grid is one-dimensional: workgroup b takes tiles b, b + gridDim.x, ...
+// (tile id = py * tiles_m + px), so that any shape launches within the
+// dispatch limits; a grid with one workgroup per tile takes one tile each.
 template <int S>
 __global__ void __launch_bounds__(256) s32_nn_kernel(const int32_t *__restrict__ lhs,
                                                      const int32_t *__restrict__ rhs,
-                                                     int32_t *__restrict__ out, int M, int N, int K) {
+                                                     int32_t *__restrict__ out, int M, int N, int K, int tiles_m,
+                                                     int64_t tiles) {
   constexpr int T = 16;
   __shared__ int32_t lhs_s[S][T][T];
   __shared__ int32_t rhs_s[S][T][T];
-  const int px = blockIdx.x, py = blockIdx.y;
   const int qx = threadIdx.x / T, qy = threadIdx.x % T;
-  const int gm = px * T + qx, gn = py * T + qy;
-  const int n_k = (K + T - 1) / T;
+  const int n_k = K / T + (K % T != 0);  // K + T - 1 could overflow
 
-  int32_t a_reg = 0, b_reg = 0;
-  auto fetch = [&](int t) {  // global -> registers
-    const int ka = t * T + qy, kb = t * T + qx;
-    a_reg = (gm < M && ka < K) ? lhs[(int64_t)gm * K + ka] : 0;
-    b_reg = (kb < K && gn < N) ? rhs[(int64_t)kb * N + gn] : 0;
-  };
-  auto put = [&](int slot) {  // registers -> LDS slot
-    lhs_s[slot][qx][qy] = a_reg;
-    rhs_s[slot][qx][qy] = b_reg;
-  };
-  uint32_t acc = 0;  // wraps modulo 2^32
-  auto mac = [&](int slot) {
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int px = (int)(tile % tiles_m), py = (int)(tile / tiles_m);
+    const int gm = px * T + qx, gn = py * T + qy;
+    int32_t a_reg = 0, b_reg = 0;
+    auto fetch = [&](int t) {  // global -> registers
+      const int ka = t * T + qy, kb = t * T + qx;
+      a_reg = (gm < M && ka < K) ? lhs[(int64_t)gm * K + ka] : 0;
+      b_reg = (kb < K && gn < N) ? rhs[(int64_t)kb * N + gn] : 0;
+    };
+    auto put = [&](int slot) {  // registers -> LDS slot
+      lhs_s[slot][qx][qy] = a_reg;
+      rhs_s[slot][qx][qy] = b_reg;
+    };
+    uint32_t acc = 0;  // wraps modulo 2^32
+    auto mac = [&](int slot) {
 #pragma unroll
-    for (int k = 0; k < T; ++k) acc += (uint32_t)lhs_s[slot][qx][k] * (uint32_t)rhs_s[slot][k][qy];
-  };
+      for (int k = 0; k < T; ++k) acc += (uint32_t)lhs_s[slot][qx][k] * (uint32_t)rhs_s[slot][k][qy];
+    };
 
-  if constexpr (S == 1) {
-    for (int t = 0; t < n_k; ++t) {
-      fetch(t);
-      put(0);
-      __syncthreads();
-      mac(0);
-      __syncthreads();
-    }
-  } else {
-    if (n_k > 0) {
-      int cur = 0, nxt = 1;
-      fetch(0);  // prologue: tile 0 into the current slot
-      put(cur);
-      __syncthreads();
-      for (int t = 1; t < n_k; ++t) {  // steady state
-        fetch(t);                      // loads of tile t in flight ...
-        mac(cur);                      // ... while tile t-1 is consumed
-        put(nxt);
+    if constexpr (S == 1) {
+      for (int t = 0; t < n_k; ++t) {
+        fetch(t);
+        put(0);
         __syncthreads();
-        const int tmp = cur;  // swap the slot names, not the bytes
-        cur = nxt;
-        nxt = tmp;
+        mac(0);
+        __syncthreads();
       }
-      mac(cur);  // epilogue: drain the last tile
+    } else {
+      if (n_k > 0) {
+        int cur = 0, nxt = 1;
+        fetch(0);  // prologue: tile 0 into the current slot
+        put(cur);
+        __syncthreads();
+        for (int t = 1; t < n_k; ++t) {  // steady state
+          fetch(t);                      // loads of tile t in flight ...
+          mac(cur);                      // ... while tile t-1 is consumed
+          put(nxt);
+          __syncthreads();
+          const int tmp = cur;  // swap the slot names, not the bytes
+          cur = nxt;
+          nxt = tmp;
+        }
+        mac(cur);  // epilogue: drain the last tile
+        // the next output tile's prologue writes slot 0, which every
+        // thread may still be reading here
+        __syncthreads();
+      }
     }
+    if (gm < M && gn < N) out[(int64_t)gm * N + gn] = (int32_t)acc;
   }
-  if (gm < M && gn < N) out[(int64_t)gm * N + gn] = (int32_t)acc;
 }
 
 // ============================================================== NT common

@@ -59,6 +59,11 @@ std::atomic<int> g_persist_mode{0};  // 0 planned, 1 never, 2 always (producer/c
 // and it measured no faster than the per-tile kernel at 4096^3 and 8192^3.
 // pgemm_set_persistent(2) selects it.
 constexpr int64_t kCUs = 256;  // compute units of an MI355X
+// A dispatch's size in work-items per dimension is a 32-bit field.  The int32
+// kernel walks its tiles from a grid of at most this many workgroups (2^28
+// work-items); an NT plan whose grid reaches 2^32 work-items is refused.
+constexpr int64_t kS32MaxGrid = (int64_t)1 << 20;
+constexpr int64_t kMaxWorkItems = (int64_t)1 << 32;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -173,7 +178,7 @@ pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, Plan
       info->consumer_waves = 4;
       info->threads = 256;
       info->lds_bytes = s * 2 * 16 * 16 * 4;
-      info->grid = cdiv(M, 16) * cdiv(N, 16);
+      info->grid = std::min<int64_t>(cdiv(M, 16) * cdiv(N, 16), kS32MaxGrid);
       info->k_tiles = cdiv(K, 16);
       info->k_split = 1;
       return PGEMM_OK;
@@ -199,6 +204,7 @@ pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, Plan
       return PGEMM_ERR_STAGES;
   }
   if (info->lds_bytes < 0 || info->lds_bytes > kLdsLimit) return PGEMM_ERR_LDS;
+  if (info->grid * info->threads >= kMaxWorkItems) return PGEMM_ERR_SHAPE;
   return PGEMM_OK;
 }
 
@@ -422,12 +428,16 @@ pgemm_status pgemm_s32_nn(const int32_t *lhs, const int32_t *rhs, int32_t *out, 
   int dev = 0;
   st = current_device(&dev);
   if (st != PGEMM_OK) return st;
-  const dim3 grid((unsigned)cdiv(M, 16), (unsigned)cdiv(N, 16));
+  const dim3 grid((unsigned)p.info.grid);
+  const int tiles_m = (int)cdiv(M, 16);
+  const int64_t tiles = cdiv(M, 16) * cdiv(N, 16);
   hipStream_t h = static_cast<hipStream_t>(stream);
   if (p.stages == 1)
-    hipLaunchKernelGGL(s32_nn_kernel<1>, grid, dim3(256), 0, h, lhs, rhs, out, (int)M, (int)N, (int)K);
+    hipLaunchKernelGGL(s32_nn_kernel<1>, grid, dim3(256), 0, h, lhs, rhs, out, (int)M, (int)N, (int)K, tiles_m,
+                       tiles);
   else
-    hipLaunchKernelGGL(s32_nn_kernel<2>, grid, dim3(256), 0, h, lhs, rhs, out, (int)M, (int)N, (int)K);
+    hipLaunchKernelGGL(s32_nn_kernel<2>, grid, dim3(256), 0, h, lhs, rhs, out, (int)M, (int)N, (int)K, tiles_m,
+                       tiles);
   return launched();
 }
 

@@ -171,6 +171,32 @@ def test_query_rejects_shapes(L):
     assert L.pgemm_query(1, 0, 64, 64, 64, None) == ERR_NULL
 
 
+def test_grid_limits(L):
+    # A dispatch counts its work-items in 32 bits.  int32: one workgroup per
+    # 16 x 16 tile up to 2^20, beyond that 2^20 workgroups walk the tiles.
+    q = pgemm.pgemm_query("s32_nn", 0, 100, 100, 8)
+    assert q["grid"] == 7 * 7
+    assert pgemm.pgemm_query("s32_nn", 0, 16384, 16384, 8)["grid"] == 1 << 20
+    assert pgemm.pgemm_query("s32_nn", 0, 16400, 16400, 8)["grid"] == 1 << 20
+    assert pgemm.pgemm_query("s32_nn", 0, 2 ** 31 - 1, 2 ** 31 - 1, 8)["grid"] == 1 << 20
+    # NT: a plan of 2^32 work-items or more is refused, one just below is not
+    info = pgemm.KernelInfo()
+    n = 2 ** 31 - 1
+    assert L.pgemm_query(pgemm.OPS["nt_ws"], 0, n, n, 8, ctypes.byref(info)) == ERR_SHAPE
+    pgemm.pgemm_set_tiling(128, 1)
+    try:
+        # 128 x 128 tiles of 512 (swap) or 384 (ws) threads
+        for op, threads in (("nt_swap", 512), ("nt_ws", 384)):
+            tiles_limit = -(-(2 ** 32) // threads)  # the first tile count that reaches 2^32
+            m = 128 * ((tiles_limit - 1) // 4096)  # 4096 tile columns, as many tile rows as fit
+            assert L.pgemm_query(pgemm.OPS[op], 0, m, 128 * 4096, 8, ctypes.byref(info)) == OK
+            assert info.grid * info.threads < 2 ** 32
+            m = 128 * cdiv(tiles_limit, 4096)
+            assert L.pgemm_query(pgemm.OPS[op], 0, m, 128 * 4096, 8, ctypes.byref(info)) == ERR_SHAPE
+    finally:
+        pgemm.pgemm_set_tiling(0, 0)
+
+
 FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
 
 
