@@ -27,7 +27,8 @@ using WsGeom = NtGeom<256, 256, (S <= 2 ? 64 : 32), S, 2, 4, 4>;
 // waits on its loads or fragment reads (5 % faster on the ragged
 // 4095 x 1000 x 1000 product than four waves of 64 x 64).
 // Producer/consumer: four consumer waves of 64 x 64 and two producer waves
-// (eight consumers of 64 x 32 measured slower).
+// (eight consumers of 64 x 32 measured slower; four producers no faster at
+// the best stage count of the skinny, ragged or 2048^3 products).
 template <int S>
 using SwapGeomSmall = NtGeom<128, 128, 64, S, 2, 4, 0, 1>;
 template <int S>
