@@ -206,7 +206,9 @@ struct NoLoads {
 // starts).  Split plans therefore start each output tile at its own K tile
 // and wrap around; the order depends on the tile only, so every variant and
 // stage count still gives the same bits for a given plan.  Unsplit plans
-// keep increasing k.
+// keep increasing k: their concurrently resident tiles share A and B panels
+// in L2 only while they walk K in step, and staggered starts measured 2-10 %
+// slower at 4096^3 and 8192^3.
 template <bool SPLIT>
 __device__ __forceinline__ int k_rotation(int bm, int bn, int n_k) {
   if (!SPLIT || n_k <= 1) return 0;
