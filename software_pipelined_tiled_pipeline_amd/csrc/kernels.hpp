@@ -426,31 +426,71 @@ __global__ void __launch_bounds__(G::THREADS)
   if (tid < 2 * S) full[tid] = 0u;  // full[0..S) and empty[0..S)
   __syncthreads();
 
-  WaveTile<T, G::WM, G::WN, G::BK, false> w;
+  using W = WaveTile<T, G::WM, G::WN, G::BK, false>;
+  W w;
   const int wm = wave / G::WGN, wn = wave % G::WGN;
+  // Consumers whose block leaves room for two fragment sets within the
+  // register budget (the 64 x 64 blocks of the 128 x 128 tile, not the
+  // 128 x 64 ones of the large tile) read the next k32 step while the
+  // current step's MFMAs run.
+  constexpr bool kTwoSets = (W::TM * W::TN + 2 * (W::TM + W::TN)) * 4 <= 144;
   if (wave < C) {
     // ---------------------------------------------------------- consumer
     if (!skip_seed)
       for (int s = 0; s < S; ++s) credit_trigger(&empty[s]);  // every slot starts free
     w.zero();
-    // `full` of the next tile's slot is read at the start of each tile and
-    // checked after its MFMAs, so a credit that has already arrived costs no
-    // LDS round trip; only a short one is waited for.
-    uint32_t seen = 0;
-    for (int t = 0; t < n_k; ++t) {
-      const int s = t % S;
-      const uint32_t target = (uint32_t)P * ((uint32_t)(t / S) + 1u);
-      if (seen < target) credit_wait(&full[s], target, max_polls, err);
-      compiler_fence();
-      const uint32_t next = t + 1 < n_k ? credit_load(&full[(t + 1) % S]) : 0u;
-      char *base = slot_ptr(s);
-      w.template mma_ktile<1>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES,
-                              lane);
-      wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
-      credit_trigger(&empty[s]);
-      seen = __builtin_amdgcn_readfirstlane(next);
+    if constexpr (kTwoSets) {
+      // The first step of tile t+1 is read during the last step of tile t,
+      // so slot t is released as soon as its last reads have landed and
+      // `full` of tile t+1 is waited for before that last step.  Every tile
+      // runs the same code, the last one included (it reads the slot after
+      // it: landed or never-written data that is no longer refilled and is
+      // never used): with a separate tail the compiler kept the accumulators
+      // in other registers there and copied them right before MFMAs, a
+      // hazard it cannot see through the inline asm.
+      static_assert(W::NK % 2 == 0, "fragment sets line up per tile");
+      constexpr int NK = W::NK;
+      const int r = W::lane_row(lane), chunk = W::lane_chunk(lane), sw = Row::swz(r);
+      auto lane_a = [&](int s) { return slot_ptr(s) + (wm * G::WM + r) * Row::ROW_BYTES; };
+      auto lane_b = [&](int s) { return slot_ptr(s) + (G::BM + wn * G::WN + r) * Row::ROW_BYTES; };
+      typename W::Frags f[2];
+      NoLoads no_load;
+      if (n_k > 0) {
+        credit_wait(&full[0], (uint32_t)P, max_polls, err);
+        W::read_frags(f[0], lane_a(0), lane_b(0), 0, chunk, sw);
+      }
+      for (int t = 0; t < n_k; ++t) {
+        const int s = t % S, s1 = (t + 1) % S;
+#pragma unroll
+        for (int kk = 0; kk + 1 < NK; ++kk)
+          w.template mixed_step<true, 0>(f[kk & 1], f[(kk + 1) & 1], lane_a(s), lane_b(s), kk + 1, chunk, sw,
+                                         no_load);
+        wait_lgkmcnt0();  // the last fragment reads of slot s are done
+        credit_trigger(&empty[s]);
+        if (t + 1 < n_k) credit_wait(&full[s1], (uint32_t)P * ((uint32_t)((t + 1) / S) + 1u), max_polls, err);
+        w.template mixed_step<true, 0>(f[(NK - 1) & 1], f[NK & 1], lane_a(s1), lane_b(s1), 0, chunk, sw, no_load);
+      }
+      w.settle();
+    } else {
+      // `full` of the next tile's slot is read at the start of each tile and
+      // checked after its MFMAs, so a credit that has already arrived costs no
+      // LDS round trip; only a short one is waited for.
+      uint32_t seen = 0;
+      for (int t = 0; t < n_k; ++t) {
+        const int s = t % S;
+        const uint32_t target = (uint32_t)P * ((uint32_t)(t / S) + 1u);
+        if (seen < target) credit_wait(&full[s], target, max_polls, err);
+        compiler_fence();
+        const uint32_t next = t + 1 < n_k ? credit_load(&full[(t + 1) % S]) : 0u;
+        char *base = slot_ptr(s);
+        w.template mma_ktile<1>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES,
+                                lane);
+        wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
+        credit_trigger(&empty[s]);
+        seen = __builtin_amdgcn_readfirstlane(next);
+      }
+      w.settle();
     }
-    w.settle();
   } else {
     // ---------------------------------------------------------- producer
     Loader ld;

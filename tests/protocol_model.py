@@ -13,7 +13,10 @@ per-wave instruction lists, the schedules that the kernels run:
   one to `full` once the loads have landed;
   consumers seed one `empty` credit per slot, wait for `full`, read the slot
   and add one to `empty`.  Credits are monotonic counters: round r of a slot
-  waits for (r + 1) x (the number of waves that add to it).
+  waits for (r + 1) x (the number of waves that add to it).  Consumers that
+  read one k32 step ahead (two fragment sets) issue the same credit events in
+  the same order and, after their last tile, read the slot after it without
+  a credit: data they never use, but a read that no write may overlap.
 
 The explorer runs every interleaving of the waves (and, for asynchronous
 loads, every moment at which an issued load may land) by depth-first search
@@ -63,7 +66,8 @@ class Result:
 
 def ws_programs(S: int, n_k: int, P: int, C: int, *, bootstrap: bool = True, early_release: bool = False,
                 producer_trips: Optional[int] = None, consumer_trips: Optional[int] = None,
-                lookahead: int = 0, no_sync: bool = False, lag: Optional[int] = None):
+                lookahead: int = 0, no_sync: bool = False, lag: Optional[int] = None,
+                read_after_last: bool = False):
     """Producer/consumer: P producers (share p of every slot), C consumers.
 
     As in the kernel, a producer issues its share of tile t as an
@@ -75,7 +79,8 @@ def ws_programs(S: int, n_k: int, P: int, C: int, *, bootstrap: bool = True, ear
     early_release adds to `empty` before the slot's reads finish; *_trips
     changes one role's trip count; lookahead=1 lets producers run one round
     ahead of their credits; lag sets another lag; no_sync drops every wait
-    and credit."""
+    and credit.  read_after_last adds the consumers' uncredited read of slot
+    n_k mod S after their last release (tile None: checked for WAR only)."""
     pt = n_k if producer_trips is None else producer_trips
     ct = n_k if consumer_trips is None else consumer_trips
     lg = max(S - 2, 0) if lag is None else lag
@@ -111,6 +116,9 @@ def ws_programs(S: int, n_k: int, P: int, C: int, *, bootstrap: bool = True, ear
             prog.append((REND, s, t))
             if not early_release and not no_sync:
                 prog.append((ADD, "empty", s))
+        if read_after_last and ct > 0:
+            prog.append((RBEGIN, ct % S, None))
+            prog.append((REND, ct % S, None))
         progs.append(prog)
     return progs, P  # shares per slot: one per producer
 
@@ -276,15 +284,16 @@ class _Explorer:
             tags = _set2(tags, s, share, t)
         elif k == RBEGIN:
             _, s, t = ins
-            if any(x != t for x in tags[s]) or any(x is not None for x in writing[s]):
+            if t is not None and (any(x != t for x in tags[s]) or any(x is not None for x in writing[s])):
                 self.flag("raw", f"read of tile {t} from slot {s} holding {tags[s]}")
             reading = _set1(reading, s, reading[s] | {w})
         elif k == REND:
             _, s, t = ins
-            if any(x != t for x in tags[s]) or any(x is not None for x in writing[s]):
+            if t is not None and (any(x != t for x in tags[s]) or any(x is not None for x in writing[s])):
                 self.flag("raw", f"slot {s} changed while tile {t} was read")
             reading = _set1(reading, s, reading[s] - {w})
-            log = _set1(log, w, log[w] + (t,))
+            if t is not None:  # a read of data that is never used is no tile read
+                log = _set1(log, w, log[w] + (t,))
         elif k == ISSUE:
             _, s, t, share = ins
             iss = list(issued)

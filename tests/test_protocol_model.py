@@ -81,6 +81,32 @@ def test_kernel_wait_constants_match_the_model():
 
 # ------------------------------------------------------ planted mistakes
 
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("n_k", [1, 2, 3, 5])
+@pytest.mark.parametrize("P,C", [(1, 1), (1, 2), (2, 2)])
+def test_ws_consumers_reading_ahead_safe_in_every_interleaving(S, n_k, P, C):
+    # consumers with two fragment sets (the 128 x 128 tile: 2 producers, 4
+    # consumers) keep the credit events in order and, after their last tile,
+    # read the slot after it with no credit
+    if P * C >= 4 and n_k >= 5 and S >= 3:
+        pytest.skip("covered by the random walks below")
+    r = check_ws(S, n_k, P, C, read_after_last=True)
+    assert r.ok, r.example
+
+
+@pytest.mark.parametrize("S,n_k", [(4, 16), (3, 12), (2, 9), (1, 8)])
+def test_ws_consumers_reading_ahead_safe_on_random_interleavings(S, n_k):
+    r = check_ws(S, n_k, 2, 4, exhaustive=False, walks=200, seed=S + n_k, read_after_last=True)
+    assert r.ok, r.example
+
+
+def test_read_after_the_last_tile_is_checked_for_overwrites():
+    # a producer running one tile more than the consumers refills the slot
+    # that the consumers read after their last tile
+    r = check_ws(2, 3, 1, 1, read_after_last=True, producer_trips=4)
+    assert r.war, r.example
+
+
 def test_missing_bootstrap_deadlocks():
     for S, P, C in [(1, 1, 1), (2, 1, 2), (4, 2, 2)]:
         r = check_ws(S, 4, P, C, bootstrap=False)
