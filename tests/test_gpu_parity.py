@@ -264,7 +264,7 @@ def w4():
 
 
 @pytest.mark.parametrize("tile", [0, 256])
-@pytest.mark.parametrize("variant,stages", [("ws", 4), ("ws", 2), ("swap", 4), ("swap", 2), ("swap", 1)])
+@pytest.mark.parametrize("variant,stages", VARIANTS)
 def test_workload_bf16_ragged_4095x1000x1000(pg, w4, variant, stages, tile):
     M, N, K = 4095, 1000, 1000
     A, B, ref, mag = w4
