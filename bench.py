@@ -448,9 +448,22 @@ def main():
             result["roofline"]["mfma_only_loop"] = loop
     if args.workload == "f16_nt_skinny":
         alg_bytes = (M * K + N * K + M * N) * 2
+        achieved_gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
         result["roofline"].update({
-            "bound": "hbm", "achieved": round(alg_bytes / (kern_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-            "unit": "GB/s", "frac": round(alg_bytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+            "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4)})
+        # what a plain device copy moves on this machine (read + write bytes per
+        # second), beside the nominal 8 TB/s
+        n = 512 << 20
+        src = torch.ones(n // 2, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        copy = lambda: dst.copy_(src)
+        time_launches(copy, 3, stream)
+        copy_ms = time_launches(copy, 5, stream)
+        copy_gbs = 2 * n / (copy_ms * 1e-3) / 1e9
+        result["roofline"]["measured_copy"] = {"bytes": 2 * n, "gbs": round(copy_gbs, 1),
+                                               "frac_of_copy": round(achieved_gbs / copy_gbs, 4)}
+        del src, dst
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of the same product")
         result["cpu_baseline"] = cpu_baseline(fmt, A, B, M, N, K, args.cpu_budget)
