@@ -9,7 +9,7 @@ finds fastest; the single-schedule kernel is swept too and reported beside it.
 
 Prints one JSON line (rank 0) with TFLOP/s, the roofline position of the
 kernel (average launch time from HIP events on the launch stream), the
-vendor library's rate on the same f16 operands (torch.matmul), the
+vendor library's rate on the same operands (torch.matmul or torch.mm), the
 rate of an MFMA-only loop of the same instruction (libpgemm_probe.so; a
 reference point for the power-limited clock, not an upper bound), and the CPU
 oracle timed on a bounded sample of the same product.  Other
@@ -362,31 +362,40 @@ def main():
     single_us = {"median": round(single[n_single // 2] * 1e3, 2), "min": round(single[0] * 1e3, 2),
                  "p90": round(single[(9 * n_single) // 10] * 1e3, 2), "launches": n_single}
 
-    # the vendor library on the same operands and stream, for context (f16
-    # only): torch.matmul with the K-contiguous rhs as a transposed view,
-    # timed after our own timed region in three alternating rounds, medians
-    # reported.  In each round either side first runs untimed for about two
-    # milliseconds: ten launches of a 0.1 ms product right after the other
-    # side's ran measurably slower (the clock settles to each kernel's power
-    # draw in about a millisecond).
-    reference = None
+    # the vendor library on the same operands and stream, for context:
+    # torch.matmul (f16) or torch.mm (bf16: a plain 2-D product, not a
+    # batched one) with the K-contiguous rhs as a transposed view, into the
+    # same preallocated output, timed after our own timed region in three
+    # alternating rounds,
+    # medians reported.  In each round either side first runs untimed for
+    # about two milliseconds: ten launches of a 0.1 ms product right after
+    # the other side's ran measurably slower (the clock settles to each
+    # kernel's power draw in about a millisecond).
     if fmt == "f16":
+        call_name = "torch.matmul (hipBLASLt)"
+
         def ref_call():
             t, a_, b_ = operands()
             torch.matmul(a_, b_.t(), out=out)
-        settle = max(3, int(2.0 / max(kern_ms, 1e-3)))
-        ref_ms, ours_ms = [], []
-        for _ in range(3):
-            time_launches(ref_call, settle, stream)
-            ref_ms.append(time_launches(ref_call, 10, stream))
-            time_launches(step, settle, stream)
-            ours_ms.append(time_launches(step, 10, stream))
-        ms_ref, ms_ours = float(np.median(ref_ms)), float(np.median(ours_ms))
-        reference = {"call": "torch.matmul (hipBLASLt)", "tflops": round(flops / (ms_ref * 1e-3) / 1e12, 1),
-                     "ours_alternating_tflops": round(flops / (ms_ours * 1e-3) / 1e12, 1)}
-        reference["ours_over_reference"] = round(ms_ref / ms_ours, 3)
-        log(f"[bench] torch.matmul: {ms_ref * 1e3:.1f} us, {reference['tflops']} TFLOP/s; ours alternating "
-            f"with it {reference['ours_alternating_tflops']} TFLOP/s")
+    else:
+        call_name = "torch.mm (hipBLASLt)"
+
+        def ref_call():
+            t, a_, b_ = operands()
+            torch.mm(a_, b_.t(), out=out)
+    settle = max(3, int(2.0 / max(kern_ms, 1e-3)))
+    ref_ms, ours_ms = [], []
+    for _ in range(3):
+        time_launches(ref_call, settle, stream)
+        ref_ms.append(time_launches(ref_call, 10, stream))
+        time_launches(step, settle, stream)
+        ours_ms.append(time_launches(step, 10, stream))
+    ms_ref, ms_ours = float(np.median(ref_ms)), float(np.median(ours_ms))
+    reference = {"call": call_name, "tflops": round(flops / (ms_ref * 1e-3) / 1e12, 1),
+                 "ours_alternating_tflops": round(flops / (ms_ours * 1e-3) / 1e12, 1)}
+    reference["ours_over_reference"] = round(ms_ref / ms_ours, 3)
+    log(f"[bench] {call_name}: {ms_ref * 1e3:.1f} us, {reference['tflops']} TFLOP/s; ours alternating "
+        f"with it {reference['ours_alternating_tflops']} TFLOP/s")
 
     # spot check of the timed output against the oracle
     import oracle
@@ -437,8 +446,7 @@ def main():
             "kernel_avg_us": round(kern_ms * 1e3, 2),
         },
     }
-    if reference:
-        result["reference_library"] = reference
+    result["reference_library"] = reference
     if args.workload != "f16_nt_skinny":
         loop = mfma_only_loop()
         if loop:

@@ -62,3 +62,5 @@ def test_ragged_workload_line():
     roof = j["roofline"]
     assert roof["bound"] == "mfma" and 0 < roof["frac"] < 1 and roof["kernel"] == "nt_ws_kernel"
     assert roof["achieved"] > 0 and roof["kernel_avg_us"] > 0
+    ref = j["reference_library"]
+    assert ref["call"].startswith("torch.mm") and ref["tflops"] > 0
