@@ -79,6 +79,22 @@ def test_kernel_wait_constants_match_the_model():
     assert "wait_vmcnt<(S - 2) * PER>();  // tile t+1 landed" in src
 
 
+def test_reading_ahead_consumer_matches_the_model():
+    # the two-fragment-set consumer of nt_ws_kernel issues, per tile, the
+    # release of slot s after its reads have landed, then the wait for `full`
+    # of the next tile, then the reads of the next tile's first step: the
+    # order that ws_programs(read_after_last=True) explores
+    src = open(KERNELS).read()
+    body = src[src.index("if constexpr (kTwoSets) {"):src.index("w.settle();", src.index("if constexpr (kTwoSets) {"))]
+    release = body.index("wait_lgkmcnt0();  // the last fragment reads of slot s are done")
+    trigger = body.index("credit_trigger(&empty[s]);", release)
+    wait_next = body.index("if (t + 1 < n_k) credit_wait(&full[s1]", trigger)
+    read_next = body.index("lane_a(s1), lane_b(s1), 0, chunk", wait_next)
+    assert release < trigger < wait_next < read_next
+    # the first tile waits for its credit before any read
+    assert body.index("credit_wait(&full[0]") < body.index("W::read_frags(f[0]")
+
+
 # ------------------------------------------------------ planted mistakes
 
 @pytest.mark.parametrize("S", [1, 2, 3, 4])
