@@ -151,6 +151,33 @@ def test_nt_random_shapes_planned(pg, fmt, M, N, K):
         assert_within_bound(fmt, got, ref, mag, f"{fmt} {variant} S={s} {M}x{N}x{K} pieces {q['k_split']}")
 
 
+def fuzz_cases(n=48, seed=20261202):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = int(rng.choice([rng.integers(1, 40), rng.integers(100, 700), rng.integers(700, 1500)]))
+        N = int(rng.choice([rng.integers(1, 40), rng.integers(100, 700), rng.integers(700, 1500)]))
+        K = 8 * int(rng.choice([rng.integers(1, 8), rng.integers(8, 80), rng.integers(80, 260)]))
+        fmt = str(rng.choice(["f16", "bf16"]))
+        variant, stages = VARIANTS[int(rng.integers(len(VARIANTS)))]
+        tile, split = [(0, 0), (128, 0), (128, 1), (128, 2), (128, 5), (256, 0), (256, 1)][int(rng.integers(7))]
+        cases.append((i, M, N, K, fmt, variant, stages, tile, split))
+    return cases
+
+
+@pytest.mark.parametrize("case", fuzz_cases(), ids=lambda c: "{}:{}x{}x{}-{}-{}{}-t{}s{}".format(*c))
+def test_nt_fuzzed_shapes_whole_output(pg, case):
+    # random shapes (ragged edges, tiny and long K), formats, variants, stage
+    # counts and forced tilings, each compared with the oracle in full
+    i, M, N, K, fmt, variant, stages, tile, split = case
+    kind = "f16_nt" if fmt == "f16" else "bf16_nt"
+    A, B = inputs.make_operands(kind, M, N, K, 7000 + i)
+    ref, mag = oracle.gemm_nt(fmt, A, B)
+    with tiling(pg, tile, split):
+        got = run_nt(pg, fmt, variant, A, B, stages)
+    assert_within_bound(fmt, got, ref, mag, f"case {case}")
+
+
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("tile,split", TILINGS)
 def test_nt_k_zero_gives_zeros(pg, fmt, tile, split):
