@@ -90,6 +90,24 @@ def test_s32_ragged_and_wrapping(pg, M, N, K, stages):
     assert np.array_equal(out.cpu().numpy(), oracle.gemm_s32_nn(A, B))
 
 
+def s32_cases(n=16, seed=99):
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(1, 700)), int(rng.integers(1, 700)), int(rng.integers(0, 300)), int(rng.integers(1, 3)))
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("case", s32_cases(), ids=lambda c: "{}:{}x{}x{}-S{}".format(*c))
+def test_s32_fuzzed_shapes(pg, case):
+    # random shapes and full-range int32 operands, bit for bit
+    i, M, N, K, stages = case
+    rng = np.random.default_rng(1000 + i)
+    A = rng.integers(-2 ** 31, 2 ** 31, (M, K)).astype(np.int32)
+    B = rng.integers(-2 ** 31, 2 ** 31, (K, N)).astype(np.int32)
+    out = pg.pgemm_s32_nn(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), stages=stages)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.gemm_s32_nn(A, B))
+
+
 # ------------------------------------------------- NT, full comparisons
 
 # K from one K tile up: at BK = 32 these give 7, 5, 1, 1, 2, 32, 3 and 4 K tiles
@@ -385,6 +403,35 @@ def test_persistent_matches_per_tile_kernel(pg, fmt, tile, M, N, K):
                 ref_bits = run_nt(pg, fmt, "ws", A, B, S, dA, dB)
             assert np.array_equal(got, ref_bits), f"persistent S={S} differs from the per-tile kernel"
     check_sampled(fmt, A, B, {"persistent": got}, 7, count=1024)
+    assert pg.pgemm_sync_status() == 0
+
+
+def persistent_cases(n=16, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        tile = int(rng.choice([128, 256]))
+        M = int(rng.integers(1, 5 * tile * 8))
+        N = int(rng.integers(1, 5 * tile * 4))
+        K = 8 * int(rng.integers(1, 100))
+        out.append((i, tile, M, N, K, str(rng.choice(["f16", "bf16"])), int(rng.integers(1, 5))))
+    return out
+
+
+@pytest.mark.parametrize("case", persistent_cases(), ids=lambda c: "{}:t{}-{}x{}x{}-{}-S{}".format(*c))
+def test_persistent_fuzzed_against_per_tile_kernel(pg, case):
+    # random shapes on both tile sizes: the persistent schedule gives the
+    # per-tile kernel's bits
+    i, tile, M, N, K, fmt, S = case
+    kind = "f16_nt" if fmt == "f16" else "bf16_nt"
+    A, B = inputs.make_operands(kind, M, N, K, 8000 + i)
+    dA, dB = dev_half(A, fmt), dev_half(B, fmt)
+    with tiling(pg, tile, 1):
+        with persistence(pg, 2):
+            got = run_nt(pg, fmt, "ws", A, B, S, dA, dB)
+        with persistence(pg, 1):
+            want = run_nt(pg, fmt, "ws", A, B, S, dA, dB)
+    assert np.array_equal(got, want)
     assert pg.pgemm_sync_status() == 0
 
 
