@@ -3,7 +3,9 @@
  *
  * Plain C interface: host or device pointers and sizes only, no HIP or torch
  * types.  Every GEMM call enqueues one kernel (two for a K-split product)
- * on the caller's HIP stream and returns without waiting for it.
+ * on the caller's HIP stream and returns without waiting for it.  No GEMM
+ * call allocates, frees or synchronises: all device memory (operands,
+ * output, the optional K-split workspace) belongs to the caller.
  *
  * Operation (Croqtile tutorial ch.6, "Synchronization: pipelines, events and
  * double buffering": the int32 listing with swap and the f16 1P1C listing
@@ -24,8 +26,10 @@
  *   - stream: a hipStream_t passed as void*; NULL is the null stream.
  *   - Errors in the arguments are reported before any HIP call is made, and
  *     nothing is enqueued.  PGEMM_ERR_LAUNCH reports a failed launch.
- *   - Calls may be made concurrently on different streams: the only state a
- *     call touches is the K-split workspace, which is per (device, stream).
+ *   - Calls may be made concurrently on different streams.  The only shared
+ *     state a call touches is the K-split workspace registered for its
+ *     (device, stream); calls on one stream from several host threads are
+ *     serialised around it by the library.
  */
 #ifndef PGEMM_H
 #define PGEMM_H
@@ -36,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PGEMM_ABI_VERSION 2
+#define PGEMM_ABI_VERSION 3
 
 typedef enum {
   PGEMM_OK = 0,
@@ -48,8 +52,7 @@ typedef enum {
   PGEMM_ERR_LDS = 5,     /* the tile ring for these stages exceeds LDS       */
   PGEMM_ERR_LAUNCH = 6,  /* the HIP launch (or a HIP query) failed           */
   PGEMM_ERR_TIMEOUT = 7, /* a credit wait exceeded its poll limit            */
-  PGEMM_ERR_DEVICE = 8,  /* the current device is not gfx950                 */
-  PGEMM_ERR_NOMEM = 9    /* the K-split workspace could not be allocated      */
+  PGEMM_ERR_DEVICE = 8   /* the current device is not gfx950                 */
 } pgemm_status;
 
 /* Variant codes used by the query functions. */
@@ -81,7 +84,13 @@ pgemm_status pgemm_s32_nn(const int32_t *lhs, const int32_t *rhs, int32_t *out,
  * the handles rotate instead of swapping).
  *   lhs: IEEE binary16 bits [M, K], rhs: binary16 bits [N, K] (row n of rhs
  *   is column n of the right operand), out: binary16 bits [M, N].
- *   K must be a multiple of 8 (else PGEMM_ERR_ALIGN) and below 2^22.
+ *   Any K below 2^31.  Rows are copied into the LDS ring with 16-byte
+ *   direct-to-LDS loads when K is a multiple of 8 and a tile's rows span
+ *   less than 2^31 bytes (tile * K < 2^30); otherwise (Croqtile ch.5,
+ *   predicated execution with `if`) with a register-staged loader whose
+ *   64-bit addressed loads are guarded element by element (elements past K
+ *   or past the matrix edge are zero).  Both fill the same ring layout, so
+ *   the two give identical bits.
  *   Products are exact and accumulate in fp32 in increasing k; the output is
  *   rounded to nearest-even.  stages: 1..4 (default 2).
  *
@@ -90,12 +99,11 @@ pgemm_status pgemm_s32_nn(const int32_t *lhs, const int32_t *rhs, int32_t *out,
  * still leaves half the CUs idle and has K >= 1024 is split along K into
  * up to 16 pieces (multiples of 64), each workgroup computing one tile over
  * one piece into an fp32 workspace, and a second kernel adds the pieces in
- * increasing order and rounds.  The workspace is allocated by the library
- * on first need, one per (device, stream), grown when a larger one is
- * needed (after synchronising that stream) and kept until the process ends;
- * PGEMM_ERR_NOMEM if it cannot be allocated.  pgemm_query reports the plan.
- * For a given plan the result is deterministic; different plans (tile size,
- * K split) may differ in the last bits.
+ * increasing order and rounds.  The split is taken only when the caller has
+ * registered a workspace of at least pgemm_query's workspace_bytes for the
+ * call's stream (pgemm_set_workspace); otherwise the call runs the same
+ * tiling unsplit.  For a given plan the result is deterministic; different
+ * plans (tile size, K split) may differ in the last bits.
  */
 pgemm_status pgemm_f16_nt(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out,
                           int64_t M, int64_t N, int64_t K, int stages, void *stream);
@@ -124,7 +132,9 @@ pgemm_status pgemm_bf16_nt_ws(const uint16_t *lhs, const uint16_t *rhs, uint16_t
  * Launch geometry the library would use for (op, stages, M, N, K), without
  * launching.  Host-only: makes no HIP call.  Returns the same argument
  * status the GEMM call would (PGEMM_ERR_STAGES, PGEMM_ERR_SHAPE,
- * PGEMM_ERR_LDS); on PGEMM_OK fills *info.
+ * PGEMM_ERR_LDS); on PGEMM_OK fills *info.  A plan with k_split > 1 is the
+ * one a call runs when its stream has a registered workspace of at least
+ * workspace_bytes; without one the call runs it with k_split 1.
  */
 typedef struct {
   int32_t block_m, block_n, block_k; /* output tile and K tile            */
@@ -138,19 +148,37 @@ typedef struct {
   int32_t k_split;                   /* K pieces; 1 = no split             */
   int32_t persistent;                /* 1: persistent schedule (see below) */
   int64_t workspace_bytes;           /* fp32 workspace of a split, else 0  */
+  int32_t staged;                    /* 1: register-staged guarded loads   */
 } pgemm_kernel_info;
 
 pgemm_status pgemm_query(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K,
                          pgemm_kernel_info *info);
 
 /*
- * Waits for `stream`, then reads and clears the device-side error word that
- * the producer/consumer kernels set when a credit wait runs past its poll
- * limit.  Returns PGEMM_ERR_TIMEOUT if any such wait gave up since the last
- * call, else PGEMM_OK (or PGEMM_ERR_LAUNCH if HIP fails).  A kernel that gave
- * up has still exited, but its output is undefined.
+ * K-split workspace (the caller owns it; Croqtile ch.5, "data-dependent and
+ * persistent grids": a launch on `stream s` only enqueues, so nothing the
+ * call needs may be allocated or awaited inside it).  Registers `bytes` of
+ * device memory at `workspace` (16-byte aligned) for later NT calls on
+ * `stream` (a hipStream_t as void*, NULL = the null stream) on the current
+ * device, replacing any earlier registration for that pair; workspace NULL
+ * with bytes 0 removes it.  The library keeps only the pointer: the caller
+ * must not free the buffer, or destroy the stream, while it is registered
+ * or while calls that used it may still run, and must not register one
+ * buffer for two streams.  Calls whose plan needs more than the registered
+ * bytes run unsplit.  PGEMM_ERR_SHAPE for bytes < 0, PGEMM_ERR_NULL for a
+ * NULL workspace with bytes > 0, PGEMM_ERR_ALIGN for a misaligned one.
  */
-pgemm_status pgemm_sync_status(void *stream);
+pgemm_status pgemm_set_workspace(void *stream, void *workspace, int64_t bytes);
+
+/*
+ * Debug status of the credit protocol.  Waits for `stream`, then reads and
+ * clears the device-side error word that the producer/consumer kernels set
+ * when a credit wait runs past its poll limit.  Returns PGEMM_ERR_TIMEOUT if
+ * any such wait gave up since the last call, else PGEMM_OK (or
+ * PGEMM_ERR_LAUNCH if HIP fails).  A kernel that gave up has still exited,
+ * but its output is undefined.  Not a GEMM call: it synchronises the host.
+ */
+pgemm_status pgemm_debug_status(void *stream);
 
 /* Tuning and test hook: forces the tiling of later NT calls in this
  * process.  tile: 0 = planned automatically, 128 or 256 = that output tile;

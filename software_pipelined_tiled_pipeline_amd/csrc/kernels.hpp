@@ -113,6 +113,7 @@ __global__ void __launch_bounds__(256) s32_nn_kernel(const int32_t *__restrict__
 template <int BM, int BN, int BK>
 struct SlotLoader {
   using Row = RingRow<BK>;
+  static constexpr bool DIRECT = true;
   static constexpr int CPR = Row::CPR;
   static constexpr int A_INSTR = BM * CPR / kWave;
   static constexpr int INSTR = (BM + BN) * CPR / kWave;
@@ -183,6 +184,115 @@ struct SlotLoader {
     (void)lane;
 #pragma unroll
     for (int i = 0; i < COUNT; ++i) load_one(slot, t, first + i, i % PAR);
+  }
+};
+
+// Register-staged fill of one ring slot, for the calls the direct path
+// cannot take: rows that do not start on 16 bytes (K not a multiple of 8),
+// and panels whose byte span passes the 32-bit offsets of a buffer resource
+// (long K).  It fills exactly the slot layout of SlotLoader (instruction j,
+// lane l -> granule 64 j + l at the same swizzled position), so consumers
+// are unchanged.  Each lane builds its 16-byte granule in registers from
+// global loads with 64-bit addresses:
+//   - K a multiple of 8: one 16-byte load per granule (a granule then lies
+//     wholly inside or wholly outside the K range);
+//   - otherwise eight 2-byte loads, each guarded by the K bound, so that an
+//     element past K is zero and never read (Croqtile ch.5, predicated
+//     execution with `if`: partial tiles are protected element by element).
+// Rows past the matrix edge are zero.  The choice between the two is made
+// once per launch (the same for every wave).  The granule is then written
+// with ds_write_b128; a load call returns with its writes issued, so the
+// LDS wait that precedes the next barrier or credit trigger covers them.
+// Tiles at or past the end of the sequence write nothing (no later read of
+// those slots is used).
+template <int BM, int BN, int BK>
+struct StagedLoader {
+  using Row = RingRow<BK>;
+  static constexpr bool DIRECT = false;
+  static constexpr int CPR = Row::CPR;
+  static constexpr int A_INSTR = BM * CPR / kWave;
+  static constexpr int INSTR = (BM + BN) * CPR / kWave;
+  static constexpr int SLOT_BYTES = (BM + BN) * Row::ROW_BYTES;
+  static constexpr int RPI = kWave / CPR;
+  static constexpr int PAR = CPR / 4;
+
+  const uint16_t *pa, *pb;  // element (row 0, column kb) of the tile's lhs / rhs rows
+  int64_t pitch;            // elements per row (the full K)
+  int rows_a, rows_b;       // rows of the tile inside the matrices
+  int klen, nk, rot;
+  bool vec;                 // K a multiple of 8: 16-byte loads
+  int lrow;                 // l / CPR: the lane's row within an instruction
+  int lane_k[PAR];          // chunk * 8 per parity, as in SlotLoader
+
+  __device__ __forceinline__ void init(const uint16_t *lhs, const uint16_t *rhs, int M, int N, int K, int kb,
+                                       int klen_, int m0, int n0, int rot_ = 0) {
+    pitch = K;
+    klen = klen_;
+    nk = (klen + BK - 1) / BK;
+    rot = rot_;
+    vec = (K & 7) == 0;
+    rows_a = M - m0 < BM ? M - m0 : BM;
+    rows_b = N - n0 < BN ? N - n0 : BN;
+    pa = lhs + (int64_t)m0 * K + kb;
+    pb = rhs + (int64_t)n0 * K + kb;
+    const int lane = threadIdx.x & (kWave - 1);
+    lrow = lane / CPR;
+#pragma unroll
+    for (int p = 0; p < PAR; ++p) lane_k[p] = ((lane % CPR) ^ Row::swz(p * RPI + lane / CPR)) * 8;
+  }
+
+  // The granule of instruction j for the t-th K tile of the sequence, in
+  // registers (zero outside the matrices).
+  __device__ __forceinline__ u32x4 fetch(int t, int j, int p) const {
+    const bool is_a = j < A_INSTR;
+    const int jj = is_a ? j : j - A_INSTR;
+    int kt = t + rot;
+    if (kt >= nk) kt -= nk;
+    const int row = jj * RPI + lrow;
+    const int k = kt * BK + lane_k[p];  // relative to the workgroup's first column
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < (is_a ? rows_a : rows_b)) {
+      const uint16_t *src = (is_a ? pa : pb) + (int64_t)row * pitch + k;
+      if (vec) {
+        if (k < klen) v = *reinterpret_cast<const u32x4 *>(src);
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = k + e < klen ? (uint32_t)src[e] : 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = h[2 * q] | (h[2 * q + 1] << 16);
+      }
+    }
+    return v;
+  }
+
+  __device__ __forceinline__ static void put(char *slot, int j, u32x4 v) {
+    const int lane = threadIdx.x & (kWave - 1);
+    *reinterpret_cast<u32x4 *>(slot + j * (kWave * 16) + lane * 16) = v;
+  }
+
+  __device__ __forceinline__ void load_one(char *slot, int t, int j, int p) const {
+    if (t >= nk) return;
+    put(slot, j, fetch(t, j, p));
+  }
+
+  // Instructions first .. first+COUNT-1 of the slot for tile t, in batches
+  // of up to four granules: a batch's global loads, then its LDS writes
+  // (four granules in flight bound the staging registers).
+  template <int COUNT>
+  __device__ __forceinline__ void load(char *slot, int t, int first, int lane) const {
+    (void)lane;
+    if (t >= nk) return;
+    constexpr int B = COUNT < 4 ? COUNT : 4;
+    static_assert(COUNT % B == 0 && B % PAR == 0, "batches keep the parity pattern");
+#pragma unroll
+    for (int b = 0; b < COUNT; b += B) {
+      u32x4 v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) v[i] = fetch(t, first + b + i, i % PAR);
+#pragma unroll
+      for (int i = 0; i < B; ++i) put(slot, first + b + i, v[i]);
+    }
   }
 };
 
@@ -279,7 +389,7 @@ struct NtGeom {
 // only step; the fragment sets then alternate per tile, so the loop body
 // covers two tiles.  S = 1 has a single slot and runs fill -> barrier ->
 // compute -> barrier.
-template <typename T, class G, bool SPLIT>
+template <typename T, class G, bool SPLIT, bool STAGED>
 __global__ void __launch_bounds__(G::THREADS, G::OCC)
     nt_swap_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
                    uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m,
@@ -289,7 +399,7 @@ __global__ void __launch_bounds__(G::THREADS, G::OCC)
   // flight when the main loop starts would turn the loop's first fragment
   // wait into a wait for every outstanding LDS read.
   __asm__ volatile("" ::"s"(out), "s"(partial), "s"(ldp));
-  using Loader = typename G::Loader;
+  using Loader = std::conditional_t<STAGED, StagedLoader<G::BM, G::BN, G::BK>, typename G::Loader>;
   using Row = RingRow<G::BK>;
   using W = WaveTile<T, G::WM, G::WN, G::BK>;
   constexpr int S = G::S;
@@ -349,8 +459,15 @@ __global__ void __launch_bounds__(G::THREADS, G::OCC)
       wait_vmcnt<(S - 2) * PER>();  // tile t+1 landed
       lds_barrier();
       const int s1 = (t + 1) % S;
-      w.template mixed_step<true, PER>(f[C], f[C ^ 1], lane_a(s1), lane_b(s1), 0, chunk, sw,
-                                       RefillLoads<Loader>{ld, slot_ptr(t % S), t + S, first});
+      if constexpr (Loader::DIRECT) {
+        w.template mixed_step<true, PER>(f[C], f[C ^ 1], lane_a(s1), lane_b(s1), 0, chunk, sw,
+                                         RefillLoads<Loader>{ld, slot_ptr(t % S), t + S, first});
+      } else {
+        // staged loads wait for their data before writing it: issued after
+        // the step's MFMAs, their latency does not stall the MFMA stream
+        w.template mixed_step<true, 0>(f[C], f[C ^ 1], lane_a(s1), lane_b(s1), 0, chunk, sw, no_load);
+        ld.template load<PER>(slot_ptr(t % S), t + S, first, lane);
+      }
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
@@ -399,14 +516,14 @@ __global__ void __launch_bounds__(G::THREADS, G::OCC)
 
 // ========================================================= NT, WS (credits)
 
-template <typename T, class G, bool SPLIT>
+template <typename T, class G, bool SPLIT, bool STAGED>
 __global__ void __launch_bounds__(G::THREADS)
     nt_ws_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
                  uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m,
                  int k_chunk, float *__restrict__ partial, int ldp, uint32_t max_polls, int skip_seed,
                  uint32_t *err) {
   static_assert(G::P > 0, "producer/consumer kernel needs producer waves");
-  using Loader = typename G::Loader;
+  using Loader = std::conditional_t<STAGED, StagedLoader<G::BM, G::BN, G::BK>, typename G::Loader>;
   using Row = RingRow<G::BK>;
   constexpr int S = G::S, C = G::CW, P = G::P;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -501,15 +618,20 @@ __global__ void __launch_bounds__(G::THREADS)
     // the loads of tile t + LAG are issued, when its own have landed.  LAG =
     // S - 2 keeps the consumers fed: the tile they need next is complete
     // once the producer holds the credit of the slot they just released.
+    // Staged loads have written the tile by the time the call returns, so
+    // `full` follows at once (LAG = 0), after the LDS writes complete.
     constexpr int PER = G::PER_LOADER;
-    constexpr int LAG = S >= 2 ? S - 2 : 0;
+    constexpr int LAG = (Loader::DIRECT && S >= 2) ? S - 2 : 0;
     static_assert((LAG + 1) * PER < 64, "loads in flight fit the 6-bit vmcnt");
     for (int t = 0; t < n_k; ++t) {
       const int s = t % S;
       credit_wait(&empty[s], (uint32_t)C * ((uint32_t)(t / S) + 1u), max_polls, err);
       ld.template load<PER>(slot_ptr(s), t, first, lane);
       if (t >= LAG) {
-        wait_vmcnt<LAG * PER>();  // tile t - LAG landed
+        if constexpr (Loader::DIRECT)
+          wait_vmcnt<LAG * PER>();  // tile t - LAG landed
+        else
+          wait_lgkmcnt0();  // this wave's writes of tile t are done
         credit_trigger(&full[(t - LAG) % S]);
       }
     }

@@ -13,6 +13,7 @@
 
 #include "pgemm.h"
 #include "instances.hpp"
+#include "launch.hpp"
 #include "planner.hpp"
 
 // Device-side error word: a credit wait that runs past its poll limit sets
@@ -25,9 +26,10 @@ using namespace pgemm;
 
 constexpr int kLdsLimit = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
-// Buffer offsets inside a 256-row panel must stay below 2^31 bytes.
-constexpr int64_t kMaxKNt = (int64_t)1 << 22;
-constexpr int kGroupM = 4;
+// The direct-to-LDS loads address a tile's panel (its rows over the K range)
+// through one buffer resource with 32-bit byte offsets that must stay below
+// 2^31: a panel of `tile` rows of K elements qualifies while tile * K < 2^30.
+constexpr int64_t kDirectPanelElems = (int64_t)1 << 30;
 constexpr uint32_t kDefaultPolls = 1u << 24;
 
 std::atomic<uint32_t> g_max_polls{kDefaultPolls};
@@ -72,6 +74,7 @@ struct Plan {
   int stages = 0;
   int split = 1;        // K pieces
   bool persistent = false;
+  bool staged = false;  // register-staged, element-guarded loads
   int64_t k_chunk = 0;  // K elements per piece (K itself without a split)
   int64_t ldp = 0;      // row pitch of the partial-sum planes, in floats
   pgemm_kernel_info info{};
@@ -116,6 +119,7 @@ void fill_nt(Plan *p, int64_t M, int64_t N) {
     i->grid = std::min<int64_t>(i->grid, kCUs * per_cu);
     i->persistent = 1;
   }
+  i->staged = p->staged ? 1 : 0;
   i->workspace_bytes = p->split > 1 ? p->split * M * p->ldp * (int64_t)sizeof(float) : 0;
 }
 
@@ -130,7 +134,13 @@ bool fill_nt_s(Plan *p, int s, int64_t M, int64_t N) {
   return false;
 }
 
-void choose_tiling(Plan *p, int64_t M, int64_t N, int64_t K) {
+int64_t split_workspace_bytes(int split, int64_t M, int64_t N) {
+  return split > 1 ? split * M * (cdiv(N, 4) * 4) * (int64_t)sizeof(float) : 0;
+}
+
+// `avail`: bytes of workspace the call can use for a K split's partial sums;
+// a split that would need more is not planned.
+void choose_tiling(Plan *p, int64_t M, int64_t N, int64_t K, int64_t avail) {
   const int force_tile = g_force_tile.load(std::memory_order_relaxed);
   const int force_split = g_force_split.load(std::memory_order_relaxed);
   const int64_t large = cdiv(M, kLargeTile) * cdiv(N, kLargeTile);
@@ -152,15 +162,18 @@ void choose_tiling(Plan *p, int64_t M, int64_t N, int64_t K) {
   if (split > 1) {
     p->k_chunk = cdiv(cdiv(K, split), kPieceAlign) * kPieceAlign;
     p->split = (int)cdiv(K, p->k_chunk);  // no empty pieces
-    if (p->split <= 1) {
+    if (p->split <= 1 || split_workspace_bytes(p->split, M, N) > avail) {
       p->split = 1;
       p->k_chunk = K;
     }
   }
   p->ldp = cdiv(N, 4) * 4;
+  // rows that do not start on 16 bytes, or a panel past the direct loads'
+  // 32-bit offsets, take the register-staged loader
+  p->staged = (K % 8) != 0 || (int64_t)p->tile * K >= kDirectPanelElems;
 }
 
-pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, Plan *p) {
+pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, int64_t avail, Plan *p) {
   if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return PGEMM_ERR_SHAPE;
   *p = Plan{};
   pgemm_kernel_info *info = &p->info;
@@ -185,13 +198,13 @@ pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, Plan
     }
     case PGEMM_OP_NT_SWAP:
     case PGEMM_OP_NT_WS: {
-      if (K >= kMaxKNt) return PGEMM_ERR_SHAPE;
       const bool ws = op == PGEMM_OP_NT_WS;
       const int s = stages == 0 ? (ws ? kWsDefaultStages : kSwapDefaultStages) : stages;
       if (s < 1 || s > (ws ? kWsMaxStages : kSwapMaxStages)) return PGEMM_ERR_STAGES;
       p->stages = s;
-      choose_tiling(p, M, N, K);
-      if (ws && p->split == 1) p->persistent = g_persist_mode.load(std::memory_order_relaxed) == 2;
+      choose_tiling(p, M, N, K, avail);
+      // the persistent kernel has the direct loader only
+      if (ws && p->split == 1 && !p->staged) p->persistent = g_persist_mode.load(std::memory_order_relaxed) == 2;
       bool ok;
       if (p->tile == kLargeTile)
         ok = ws ? fill_nt_s<WsGeom>(p, s, M, N) : fill_nt_s<SwapGeom>(p, s, M, N);
@@ -240,19 +253,6 @@ pgemm_status current_device(int *dev_out) {
   return PGEMM_OK;
 }
 
-// Raises the dynamic-LDS limit of a kernel instance once per device;
-// `done_mask` is that instance's own record of the devices already set.
-template <typename Kern>
-pgemm_status allow_lds(Kern kern, int bytes, int dev, std::atomic<uint64_t> &done_mask) {
-  const uint64_t bit = 1ull << dev;
-  if (done_mask.load(std::memory_order_acquire) & bit) return PGEMM_OK;
-  if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          bytes) != hipSuccess)
-    return PGEMM_ERR_LAUNCH;
-  done_mask.fetch_or(bit, std::memory_order_acq_rel);
-  return PGEMM_OK;
-}
-
 bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 // Pointer rules: a pointer may be NULL only when the matrix it addresses is
@@ -267,150 +267,85 @@ pgemm_status launched() { return hipGetLastError() == hipSuccess ? PGEMM_OK : PG
 
 // ------------------------------------------------------------ workspace
 //
-// fp32 partial sums of K-split products: one buffer per (device, stream),
-// grown on demand and kept until the process ends, so that launches on
-// different streams never share one and launches on one stream are ordered.
+// fp32 partial sums of K-split products live in a buffer the caller owns and
+// registers per (device, stream) with pgemm_set_workspace.  A GEMM call
+// never allocates, frees or waits: without a registered buffer large enough
+// for the split, it runs the same tiling unsplit.  The registry lock is held
+// from the lookup until the call's two kernels are enqueued, so that calls
+// made on one stream by several host threads cannot interleave their
+// kernels on the shared buffer.
 struct Workspace {
   int dev;
   void *stream;
   float *ptr;
-  size_t bytes;
+  int64_t bytes;
 };
 std::mutex g_work_mutex;
 std::vector<Workspace> g_work;
 
-pgemm_status workspace(int dev, hipStream_t stream, size_t bytes, float **out) {
-  std::lock_guard<std::mutex> lock(g_work_mutex);
-  Workspace *w = nullptr;
-  for (auto &e : g_work)
-    if (e.dev == dev && e.stream == static_cast<void *>(stream)) w = &e;
-  if (!w) {
-    g_work.push_back(Workspace{dev, static_cast<void *>(stream), nullptr, 0});
-    w = &g_work.back();
-  }
-  if (w->bytes < bytes) {
-    if (w->ptr) {
-      // earlier launches on this stream may still read the old buffer
-      if (hipStreamSynchronize(stream) != hipSuccess) return PGEMM_ERR_LAUNCH;
-      if (hipFree(w->ptr) != hipSuccess) return PGEMM_ERR_LAUNCH;
-      w->ptr = nullptr;
-      w->bytes = 0;
-    }
-    void *p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) {
-      (void)hipGetLastError();
-      return PGEMM_ERR_NOMEM;
-    }
-    w->ptr = static_cast<float *>(p);
-    w->bytes = bytes;
-  }
-  *out = w->ptr;
-  return PGEMM_OK;
+// Caller holds g_work_mutex.
+const Workspace *find_workspace(int dev, void *stream) {
+  for (const auto &e : g_work)
+    if (e.dev == dev && e.stream == stream) return &e;
+  return nullptr;
 }
 
 // --------------------------------------------------------------- launch
 
-struct NtArgs {
-  const uint16_t *lhs, *rhs;
-  uint16_t *out;
-  int M, N, K;
-  hipStream_t stream;
-  int dev;
-};
+enum class Elem { F16, BF16 };
 
-template <typename T, class G, bool SPLIT, bool WS>
-pgemm_status launch_nt(const NtArgs &a, const Plan &p, float *part) {
-  static std::atomic<uint64_t> lds_set{0};
-  const int tm = (int)cdiv(a.M, G::BM), tn = (int)cdiv(a.N, G::BN);
-  const dim3 grid((unsigned)((int64_t)tm * tn * p.split));
-  const int k_chunk = (int)p.k_chunk, ldp = (int)p.ldp;
-  if constexpr (WS) {
-    auto kern = nt_ws_kernel<T, G, SPLIT>;
-    pgemm_status st = allow_lds(kern, G::LDS_BYTES, a.dev, lds_set);
-    if (st != PGEMM_OK) return st;
-    const uint32_t polls = g_max_polls.load(std::memory_order_relaxed);
-    const int skip = g_skip_seed.load(std::memory_order_relaxed);
-    hipLaunchKernelGGL(kern, grid, dim3(G::THREADS), G::LDS_BYTES, a.stream, a.lhs, a.rhs, a.out, a.M, a.N, a.K, tm,
-                       tn, kGroupM, k_chunk, part, ldp, polls, skip, g_err_ptr[a.dev]);
-  } else {
-    auto kern = nt_swap_kernel<T, G, SPLIT>;
-    pgemm_status st = allow_lds(kern, G::LDS_BYTES, a.dev, lds_set);
-    if (st != PGEMM_OK) return st;
-    hipLaunchKernelGGL(kern, grid, dim3(G::THREADS), G::LDS_BYTES, a.stream, a.lhs, a.rhs, a.out, a.M, a.N, a.K, tm,
-                       tn, kGroupM, k_chunk, part, ldp);
-  }
-  pgemm_status st = launched();
-  if (st != PGEMM_OK || !SPLIT) return st;
-  int64_t blocks = cdiv((int64_t)a.M * (p.ldp / 4), 256);
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(reduce_splits<T>, dim3((unsigned)blocks), dim3(256), 0, a.stream, part, a.out, a.M, a.N, ldp,
-                     p.split);
-  return launched();
+pgemm_status launch(Elem e, const NtLaunch &a, bool staged) {
+  if (e == Elem::F16) return staged ? launch_f16_staged(a) : launch_f16_direct(a);
+  return staged ? launch_bf16_staged(a) : launch_bf16_direct(a);
 }
 
-template <typename T, class G>
-pgemm_status launch_ws_persistent(const NtArgs &a, const Plan &p) {
-  static std::atomic<uint64_t> lds_set{0};
-  auto kern = nt_ws_persistent_kernel<T, G>;
-  pgemm_status st = allow_lds(kern, G::LDS_BYTES, a.dev, lds_set);
-  if (st != PGEMM_OK) return st;
-  const int tm = (int)cdiv(a.M, G::BM), tn = (int)cdiv(a.N, G::BN);
-  const uint32_t polls = g_max_polls.load(std::memory_order_relaxed);
-  const int skip = g_skip_seed.load(std::memory_order_relaxed);
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.info.grid), dim3(G::THREADS), G::LDS_BYTES, a.stream, a.lhs, a.rhs, a.out,
-                     a.M, a.N, a.K, tm, tn, kGroupM, polls, skip, g_err_ptr[a.dev]);
-  return launched();
-}
-
-template <typename T, template <int> class Geo>
-pgemm_status launch_ws_persistent_s(const NtArgs &a, const Plan &p) {
-  switch (p.stages) {
-    case 1: return launch_ws_persistent<T, Geo<1>>(a, p);
-    case 2: return launch_ws_persistent<T, Geo<2>>(a, p);
-    case 3: return launch_ws_persistent<T, Geo<3>>(a, p);
-    case 4: return launch_ws_persistent<T, Geo<4>>(a, p);
-  }
-  return PGEMM_ERR_STAGES;
-}
-
-template <typename T, template <int> class Geo, bool SPLIT, bool WS>
-pgemm_status launch_nt_s(const NtArgs &a, const Plan &p, float *part) {
-  switch (p.stages) {
-    case 1: return launch_nt<T, Geo<1>, SPLIT, WS>(a, p, part);
-    case 2: return launch_nt<T, Geo<2>, SPLIT, WS>(a, p, part);
-    case 3: return launch_nt<T, Geo<3>, SPLIT, WS>(a, p, part);
-    case 4: return launch_nt<T, Geo<4>, SPLIT, WS>(a, p, part);
-  }
-  return PGEMM_ERR_STAGES;
-}
-
-template <typename T>
-pgemm_status nt_entry(pgemm_op op, const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int64_t M, int64_t N,
-                      int64_t K, int stages, void *stream) {
+pgemm_status nt_entry(Elem e, pgemm_op op, const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int64_t M,
+                      int64_t N, int64_t K, int stages, void *stream) {
   pgemm_status st = check_ptrs(lhs, rhs, out, M, N, K);
   if (st != PGEMM_OK) return st;
   Plan p;
-  st = plan(op, stages, M, N, K, &p);
+  st = plan(op, stages, M, N, K, INT64_MAX, &p);  // argument checks (the split is settled below)
   if (st != PGEMM_OK) return st;
-  if (K % 8 != 0) return PGEMM_ERR_ALIGN;  // rows of lhs/rhs must start on 16 bytes
   if (M == 0 || N == 0) return PGEMM_OK;
-  NtArgs a{lhs, rhs, out, (int)M, (int)N, (int)K, static_cast<hipStream_t>(stream), 0};
-  st = current_device(&a.dev);
+  int dev = 0;
+  st = current_device(&dev);
   if (st != PGEMM_OK) return st;
-  const bool ws = op == PGEMM_OP_NT_WS;
-  if (p.persistent)
-    return p.tile == kLargeTile ? launch_ws_persistent_s<T, WsGeom>(a, p) : launch_ws_persistent_s<T, WsGeomSmall>(a, p);
-  if (p.tile == kLargeTile)
-    return ws ? launch_nt_s<T, WsGeom, false, true>(a, p, nullptr)
-              : launch_nt_s<T, SwapGeom, false, false>(a, p, nullptr);
-  if (p.split == 1)
-    return ws ? launch_nt_s<T, WsGeomSmall, false, true>(a, p, nullptr)
-              : launch_nt_s<T, SwapGeomSmall, false, false>(a, p, nullptr);
+  std::unique_lock<std::mutex> lock;
   float *part = nullptr;
-  st = workspace(a.dev, a.stream, (size_t)p.info.workspace_bytes, &part);
-  if (st != PGEMM_OK) return st;
-  return ws ? launch_nt_s<T, WsGeomSmall, true, true>(a, p, part)
-            : launch_nt_s<T, SwapGeomSmall, true, false>(a, p, part);
+  if (p.split > 1) {
+    lock = std::unique_lock<std::mutex>(g_work_mutex);
+    const Workspace *w = find_workspace(dev, stream);
+    const int64_t avail = w ? w->bytes : 0;
+    if (avail < p.info.workspace_bytes) {
+      st = plan(op, stages, M, N, K, avail, &p);  // the same tiling, unsplit
+      if (st != PGEMM_OK) return st;
+      lock.unlock();
+    } else {
+      part = w->ptr;
+    }
+  }
+  NtLaunch a{};
+  a.lhs = lhs;
+  a.rhs = rhs;
+  a.out = out;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.tile = p.tile;
+  a.stages = p.stages;
+  a.split = p.split;
+  a.k_chunk = (int)p.k_chunk;
+  a.ldp = (int)p.ldp;
+  a.ws = op == PGEMM_OP_NT_WS;
+  a.persistent = p.persistent;
+  a.grid = p.info.grid;
+  a.part = part;
+  a.stream = static_cast<hipStream_t>(stream);
+  a.dev = dev;
+  a.polls = g_max_polls.load(std::memory_order_relaxed);
+  a.skip_seed = g_skip_seed.load(std::memory_order_relaxed);
+  a.err = g_err_ptr[dev];
+  return launch(e, a, p.staged);
 }
 
 }  // namespace
@@ -422,7 +357,7 @@ pgemm_status pgemm_s32_nn(const int32_t *lhs, const int32_t *rhs, int32_t *out, 
   pgemm_status st = check_ptrs(lhs, rhs, out, M, N, K);
   if (st != PGEMM_OK) return st;
   Plan p;
-  st = plan(PGEMM_OP_S32_NN, stages, M, N, K, &p);
+  st = plan(PGEMM_OP_S32_NN, stages, M, N, K, 0, &p);
   if (st != PGEMM_OK) return st;
   if (M == 0 || N == 0) return PGEMM_OK;
   int dev = 0;
@@ -443,30 +378,46 @@ pgemm_status pgemm_s32_nn(const int32_t *lhs, const int32_t *rhs, int32_t *out, 
 
 pgemm_status pgemm_f16_nt(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int64_t M, int64_t N, int64_t K,
                           int stages, void *stream) {
-  return nt_entry<_Float16>(PGEMM_OP_NT_SWAP, lhs, rhs, out, M, N, K, stages, stream);
+  return nt_entry(Elem::F16, PGEMM_OP_NT_SWAP, lhs, rhs, out, M, N, K, stages, stream);
 }
 
 pgemm_status pgemm_f16_nt_ws(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int64_t M, int64_t N,
                              int64_t K, int stages, void *stream) {
-  return nt_entry<_Float16>(PGEMM_OP_NT_WS, lhs, rhs, out, M, N, K, stages, stream);
+  return nt_entry(Elem::F16, PGEMM_OP_NT_WS, lhs, rhs, out, M, N, K, stages, stream);
 }
 
 pgemm_status pgemm_bf16_nt(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int64_t M, int64_t N, int64_t K,
                            int stages, void *stream) {
-  return nt_entry<__bf16>(PGEMM_OP_NT_SWAP, lhs, rhs, out, M, N, K, stages, stream);
+  return nt_entry(Elem::BF16, PGEMM_OP_NT_SWAP, lhs, rhs, out, M, N, K, stages, stream);
 }
 
 pgemm_status pgemm_bf16_nt_ws(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int64_t M, int64_t N,
                               int64_t K, int stages, void *stream) {
-  return nt_entry<__bf16>(PGEMM_OP_NT_WS, lhs, rhs, out, M, N, K, stages, stream);
+  return nt_entry(Elem::BF16, PGEMM_OP_NT_WS, lhs, rhs, out, M, N, K, stages, stream);
 }
 
 pgemm_status pgemm_query(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, pgemm_kernel_info *info) {
   if (!info) return PGEMM_ERR_NULL;
   Plan p;
-  pgemm_status st = plan(op, stages, M, N, K, &p);
+  pgemm_status st = plan(op, stages, M, N, K, INT64_MAX, &p);
   if (st == PGEMM_OK) *info = p.info;
   return st;
+}
+
+pgemm_status pgemm_set_workspace(void *stream, void *workspace, int64_t bytes) {
+  if (bytes < 0) return PGEMM_ERR_SHAPE;
+  if (bytes > 0 && !workspace) return PGEMM_ERR_NULL;
+  if (workspace && misaligned(workspace)) return PGEMM_ERR_ALIGN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PGEMM_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_work_mutex);
+  for (size_t i = 0; i < g_work.size(); ++i)
+    if (g_work[i].dev == dev && g_work[i].stream == stream) {
+      g_work.erase(g_work.begin() + (std::ptrdiff_t)i);
+      break;
+    }
+  if (workspace && bytes > 0) g_work.push_back(Workspace{dev, stream, static_cast<float *>(workspace), bytes});
+  return PGEMM_OK;
 }
 
 pgemm_status pgemm_set_tiling(int tile, int k_split) {
@@ -523,7 +474,7 @@ pgemm_status pgemm_set_persistent(int mode) {
   return PGEMM_OK;
 }
 
-pgemm_status pgemm_sync_status(void *stream) {
+pgemm_status pgemm_debug_status(void *stream) {
   int dev = 0;
   pgemm_status st = current_device(&dev);
   if (st != PGEMM_OK) return st;
@@ -551,12 +502,11 @@ const char *pgemm_strerror(pgemm_status status) {
     case PGEMM_ERR_NULL: return "a required pointer is NULL";
     case PGEMM_ERR_SHAPE: return "M, N or K out of range, or an unsupported tiling request";
     case PGEMM_ERR_STAGES: return "unsupported number of stages";
-    case PGEMM_ERR_ALIGN: return "pointer not 16-byte aligned, or K not a multiple of 8 for an NT call";
+    case PGEMM_ERR_ALIGN: return "pointer not 16-byte aligned";
     case PGEMM_ERR_LDS: return "tile ring exceeds the LDS budget";
     case PGEMM_ERR_LAUNCH: return "HIP launch or query failed";
     case PGEMM_ERR_TIMEOUT: return "a credit wait exceeded its poll limit";
     case PGEMM_ERR_DEVICE: return "current device is not gfx950";
-    case PGEMM_ERR_NOMEM: return "could not allocate the K-split workspace";
   }
   return "unknown status";
 }

@@ -5,6 +5,11 @@ passes their device pointers and the current HIP stream to the library
 function of the same name, and raises ``PgemmError`` on a non-zero status.
 All arithmetic runs in the library's HIP kernels; there is no other path:
 if ``libpgemm.so`` has not been built, every call raises.
+
+The library never allocates.  For a product the planner splits along K, the
+NT functions here first make sure the stream has a registered fp32
+workspace of the planned size: a torch tensor allocated on that stream and
+handed to ``pgemm_set_workspace`` (torch is the device-memory provider).
 """
 from __future__ import annotations
 
@@ -17,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libpgemm.so")
 STATUS = {
     0: "PGEMM_OK", 1: "PGEMM_ERR_NULL", 2: "PGEMM_ERR_SHAPE", 3: "PGEMM_ERR_STAGES",
     4: "PGEMM_ERR_ALIGN", 5: "PGEMM_ERR_LDS", 6: "PGEMM_ERR_LAUNCH", 7: "PGEMM_ERR_TIMEOUT",
-    8: "PGEMM_ERR_DEVICE", 9: "PGEMM_ERR_NOMEM",
+    8: "PGEMM_ERR_DEVICE",
 }
 OPS = {"s32_nn": 0, "nt_swap": 1, "nt_ws": 2}
 GEMM_SYMBOLS = ("pgemm_s32_nn", "pgemm_f16_nt", "pgemm_f16_nt_ws", "pgemm_bf16_nt", "pgemm_bf16_nt_ws")
@@ -33,7 +38,7 @@ class KernelInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "block_m", "block_n", "block_k", "stages", "producer_waves", "consumer_waves", "threads", "lds_bytes")] + [
         ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("k_split", ctypes.c_int32),
-        ("persistent", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
+        ("persistent", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64), ("staged", ctypes.c_int32)]
 
 
 _lib = None
@@ -53,8 +58,10 @@ def lib() -> ctypes.CDLL:
             f.restype = I
         L.pgemm_query.argtypes = [I, I, I64, I64, I64, ctypes.POINTER(KernelInfo)]
         L.pgemm_query.restype = I
-        L.pgemm_sync_status.argtypes = [P]
-        L.pgemm_sync_status.restype = I
+        L.pgemm_debug_status.argtypes = [P]
+        L.pgemm_debug_status.restype = I
+        L.pgemm_set_workspace.argtypes = [P, P, I64]
+        L.pgemm_set_workspace.restype = I
         L.pgemm_set_tiling.argtypes = [I, I]
         L.pgemm_set_tiling.restype = I
         L.pgemm_set_persistent.argtypes = [I]
@@ -97,9 +104,14 @@ def _call(name, lhs, rhs, out, M, N, K, stages, stream):
 
 def _operands(lhs, rhs, out, dtype, nn: bool):
     import torch
+    if not torch.cuda.is_available():
+        raise ValueError("pgemm needs a GPU")
+    here = torch.device("cuda", torch.cuda.current_device())
     for t in (lhs, rhs):
         if t.dtype != dtype or t.dim() != 2 or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"operands must be contiguous 2-D {dtype} CUDA tensors")
+        if t.device != here:
+            raise ValueError(f"operands must be on the current device {here}, not {t.device}")
     M, K = lhs.shape
     if nn:
         K2, N = rhs.shape
@@ -108,10 +120,44 @@ def _operands(lhs, rhs, out, dtype, nn: bool):
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
     if out is None:
-        out = torch.empty((M, N), dtype=dtype, device=lhs.device)
+        out = torch.empty((M, N), dtype=dtype, device=here)
     elif out.dtype != dtype or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [M, N] tensor of the operand type")
+    elif not out.is_cuda or out.device != here:
+        raise ValueError(f"out must be on the current device {here}")
     return out, M, N, K
+
+
+# (device index, stream handle) -> the uint8 tensor registered as that
+# stream's K-split workspace
+_workspaces = {}
+
+
+def ensure_workspace(nbytes: int, stream=None):
+    """Registers a workspace of at least `nbytes` for `stream` (default: the
+    current stream) on the current device, growing the registered one if it
+    is smaller; returns the tensor.  It is allocated on that stream, so that
+    torch reuses a replaced buffer only for later work on the same stream."""
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    key = (torch.cuda.current_device(), s.cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        with torch.cuda.stream(s):
+            ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device="cuda")
+        _check(lib().pgemm_set_workspace(ctypes.c_void_p(s.cuda_stream), ctypes.c_void_p(ws.data_ptr()),
+                                         ws.numel()), "pgemm_set_workspace")
+        _workspaces[key] = ws
+    return ws
+
+
+def release_workspace(stream=None) -> None:
+    """Unregisters the workspace of `stream` (after the work that used it)."""
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    key = (torch.cuda.current_device(), s.cuda_stream)
+    _check(lib().pgemm_set_workspace(ctypes.c_void_p(s.cuda_stream), None, 0), "pgemm_set_workspace")
+    _workspaces.pop(key, None)
 
 
 def pgemm_s32_nn(lhs, rhs, out=None, stages: int = 0, stream=None):
@@ -122,12 +168,19 @@ def pgemm_s32_nn(lhs, rhs, out=None, stages: int = 0, stream=None):
 
 
 def _nt(name, dtype_name):
-    def fn(lhs, rhs, out=None, stages: int = 0, stream=None):
+    op = "nt_ws" if name.endswith("_ws") else "nt_swap"
+
+    def fn(lhs, rhs, out=None, stages: int = 0, stream=None, split: bool = True):
         import torch
         out, M, N, K = _operands(lhs, rhs, out, getattr(torch, dtype_name), nn=False)
+        if split and M and N:
+            need = pgemm_query(op, stages, M, N, K)["workspace_bytes"]
+            if need:
+                ensure_workspace(need, stream)
         return _call(name, lhs, rhs, out, M, N, K, stages, stream)
     fn.__name__ = name
-    fn.__doc__ = f"{dtype_name} out[M,N] = lhs[M,K] @ rhs[N,K]^T with fp32 accumulation (library call {name})."
+    fn.__doc__ = (f"{dtype_name} out[M,N] = lhs[M,K] @ rhs[N,K]^T with fp32 accumulation (library call {name}); "
+                  "split=False leaves the stream's workspace as it is (a call without one runs unsplit).")
     return fn
 
 
@@ -143,8 +196,8 @@ def pgemm_query(op: str, stages: int, M: int, N: int, K: int) -> dict:
     return {n: getattr(info, n) for n, _ in KernelInfo._fields_}
 
 
-def pgemm_sync_status(stream=None) -> int:
-    return lib().pgemm_sync_status(_stream(stream))
+def pgemm_debug_status(stream=None) -> int:
+    return lib().pgemm_debug_status(_stream(stream))
 
 
 def pgemm_set_tiling(tile: int = 0, k_split: int = 0) -> None:

@@ -35,24 +35,9 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), n
 
 
-def test_probe_library_exports_its_header():
-    lib = os.path.join(os.path.dirname(pgemm.LIB_PATH), "libpgemm_probe.so")
-    P = ctypes.CDLL(lib)
-    names = declared_functions(os.path.join(ROOT, "include", "pgemm_probe.h"))
-    assert names == ["pgemm_probe_mfma"]
-    for n in names:
-        assert hasattr(P, n), n
-    # argument errors are reported before any HIP call
-    f = P.pgemm_probe_mfma
-    f.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
-    t, g = ctypes.c_double(), ctypes.c_double()
-    assert f(0, 0, ctypes.byref(t), ctypes.byref(g)) == 1
-    assert f(0, 100, None, ctypes.byref(g)) == 1
-
-
 def test_version_and_messages(L):
-    assert pgemm.abi_version() == 2
-    for code in range(10):
+    assert pgemm.abi_version() == 3
+    for code in range(9):
         assert pgemm.strerror(code) and pgemm.strerror(code) != "unknown status"
     assert pgemm.strerror(99) == "unknown status"
 
@@ -166,8 +151,9 @@ def test_query_rejects_shapes(L):
     info = pgemm.KernelInfo()
     assert L.pgemm_query(1, 0, -1, 64, 64, ctypes.byref(info)) == ERR_SHAPE
     assert L.pgemm_query(1, 0, 64, 2 ** 31, 64, ctypes.byref(info)) == ERR_SHAPE
-    assert L.pgemm_query(2, 0, 64, 64, 2 ** 22, ctypes.byref(info)) == ERR_SHAPE
-    assert L.pgemm_query(0, 0, 64, 64, 2 ** 22, ctypes.byref(info)) == OK
+    assert L.pgemm_query(1, 0, 64, 64, 2 ** 31, ctypes.byref(info)) == ERR_SHAPE
+    for op in (0, 1, 2):  # any K below 2^31
+        assert L.pgemm_query(op, 0, 64, 64, 2 ** 31 - 1, ctypes.byref(info)) == OK
     assert L.pgemm_query(1, 0, 64, 64, 64, None) == ERR_NULL
 
 
@@ -212,9 +198,49 @@ def test_argument_errors_before_any_hip_call(L, name):
     assert f(FAKE, FAKE, FAKE, -1, 64, 64, 0, None) == ERR_SHAPE
     assert f(FAKE, FAKE, FAKE, 64, 64, 2 ** 31, 0, None) == ERR_SHAPE
     assert f(FAKE, FAKE, FAKE, 64, 64, 64, 7, None) == ERR_STAGES
-    if nt:
-        assert f(FAKE, FAKE, FAKE, 64, 64, 12, 0, None) == ERR_ALIGN  # K not a multiple of 8
     # empty outputs: nothing to launch; pointers to empty matrices may be NULL
     assert f(None, FAKE, None, 0, 64, 64, 0, None) == OK
     assert f(FAKE, None, None, 64, 0, 64, 0, None) == OK
     assert f(None, None, None, 0, 0, 64, 0, None) == OK
+
+
+@pytest.mark.parametrize("op", ["nt_swap", "nt_ws"])
+def test_loader_choice(L, op):
+    # 16-byte direct-to-LDS loads when every row starts on 16 bytes and a
+    # tile's rows span less than 2^31 bytes; the staged loader otherwise
+    for K in (8, 1000, 4096, 8192):
+        assert pgemm.pgemm_query(op, 0, 8192, 8192, K)["staged"] == 0
+    for K in range(1, 16):
+        assert pgemm.pgemm_query(op, 0, 300, 200, K)["staged"] == int(K % 8 != 0)
+    for K in (1001, 4095, 2 ** 22 + 1):
+        assert pgemm.pgemm_query(op, 0, 4095, 1000, K)["staged"] == 1
+    # panel span: tile * K < 2^30 elements
+    pgemm.pgemm_set_tiling(256, 1)
+    try:
+        assert pgemm.pgemm_query(op, 0, 256, 256, 2 ** 22 - 8)["staged"] == 0
+        assert pgemm.pgemm_query(op, 0, 256, 256, 2 ** 22)["staged"] == 1
+    finally:
+        pgemm.pgemm_set_tiling(0, 0)
+    pgemm.pgemm_set_tiling(128, 1)
+    try:
+        assert pgemm.pgemm_query(op, 0, 256, 256, 2 ** 22)["staged"] == 0
+        assert pgemm.pgemm_query(op, 0, 256, 256, 2 ** 23)["staged"] == 1
+    finally:
+        pgemm.pgemm_set_tiling(0, 0)
+
+
+def test_staged_plans_keep_the_per_tile_kernel(L):
+    pgemm.pgemm_set_persistent(2)
+    try:
+        assert pgemm.pgemm_query("nt_ws", 0, 8192, 8192, 8192)["persistent"] == 1
+        q = pgemm.pgemm_query("nt_ws", 0, 8192, 8192, 8190)
+        assert q["staged"] == 1 and q["persistent"] == 0
+    finally:
+        pgemm.pgemm_set_persistent(0)
+
+
+def test_set_workspace_argument_errors(L):
+    # checked before any HIP call
+    assert L.pgemm_set_workspace(None, FAKE, -1) == ERR_SHAPE
+    assert L.pgemm_set_workspace(None, None, 64) == ERR_NULL
+    assert L.pgemm_set_workspace(None, FAKE + 4, 64) == ERR_ALIGN

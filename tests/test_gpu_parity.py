@@ -2,12 +2,12 @@
 
 int32 results must be bit-exact.  f16/bf16 results must satisfy, element by
 element, |gpu - ref| <= 1e-3 * sum_k |a*b| + ulp(RNE(ref)) in the output
-type, with ref and sum_k |a*b| from the binary64 oracle.  Small shapes are
-compared in full; the full-size workloads are compared on sampled elements
-(the oracle computes each one alone) plus whole edge rows and columns, and
-across stages, variants and tile sizes for bit identity (every kernel
-accumulates the k32 MFMA steps of an element in the same order; only a K
-split changes the order, into per-piece sums added in piece order).
+type, with ref and sum_k |a*b| from the binary64 oracle.  Every output,
+the full-size workloads included, is compared with the oracle element by
+element over the whole matrix; results are also compared across stages,
+variants and tile sizes for bit identity (every kernel accumulates the k32
+MFMA steps of an element in the same order; only a K split changes the
+order, into per-piece sums added in piece order).
 """
 import contextlib
 
@@ -242,32 +242,16 @@ def _closed_forms(pg, variant, stages):
 
 # ------------------------------------------------------ full-size workloads
 
-def sample_entries(M, N, count, seed):
-    rng = np.random.default_rng(seed)
-    mi = [rng.integers(0, M, count)]
-    ni = [rng.integers(0, N, count)]
-    for m in sorted({0, M - 1}):          # whole first and last rows
-        mi.append(np.full(N, m))
-        ni.append(np.arange(N))
-    for n in sorted({0, N - 1}):          # whole first and last columns
-        mi.append(np.arange(M))
-        ni.append(np.full(M, n))
-    return np.concatenate(mi), np.concatenate(ni)
-
-
-def check_sampled(fmt, A, B, outs, seed, count=2048):
-    M, N = A.shape[0], B.shape[0]
-    mi, ni = sample_entries(M, N, count, seed)
-    ref, mag = oracle.gemm_nt_entries(fmt, A, B, mi, ni)
-    worst = 0.0
-    for what, got in outs.items():
-        worst = max(worst, assert_within_bound(fmt, got[mi, ni], ref, mag, what))
-    return worst
-
-
 @pytest.fixture(scope="module")
 def w2():
     return inputs.make_operands("f16_nt", 4096, 4096, 4096, inputs.workload_seed(2))
+
+
+def check_whole(fmt, A, B, outs):
+    """Every element of every output against the oracle."""
+    ref, mag = oracle.gemm_nt(fmt, A, B)
+    for what, got in outs.items():
+        assert_within_bound(fmt, got, ref, mag, what)
 
 
 def test_workload_f16_4096_swap2_vs_ws4(pg, w2):
@@ -277,7 +261,7 @@ def test_workload_f16_4096_swap2_vs_ws4(pg, w2):
         "swap S=2": run_nt(pg, "f16", "swap", A, B, 2, dA, dB),
         "ws S=4": run_nt(pg, "f16", "ws", A, B, 4, dA, dB),
     }
-    check_sampled("f16", A, B, outs, 2)
+    check_whole("f16", A, B, outs)
     assert np.array_equal(outs["swap S=2"], outs["ws S=4"])
 
 
@@ -294,7 +278,7 @@ def test_workload_f16_8192_stage_sweep(pg):
     dA, dB = dev_half(A, "f16"), dev_half(B, "f16")
     outs = {f"ws S={s}": run_nt(pg, "f16", "ws", A, B, s, dA, dB) for s in (1, 2, 3, 4)}
     outs.update({f"swap S={s}": run_nt(pg, "f16", "swap", A, B, s, dA, dB) for s in (1, 2, 3, 4)})
-    check_sampled("f16", A, B, outs, 3, count=1024)
+    check_whole("f16", A, B, outs)
     first = outs["ws S=1"]
     for k, v in outs.items():
         assert np.array_equal(v, first), f"{k} differs in bits from ws S=1"
@@ -335,7 +319,7 @@ def test_workload_f16_skinny_128x8192x16384(pg):
         unsplit = run_nt(pg, "f16", "ws", A, B, 4, dA, dB)
     with tiling(pg, 256, 0):
         large = run_nt(pg, "f16", "swap", A, B, 2, dA, dB)
-    check_sampled("f16", A, B, dict(outs, unsplit=unsplit, large=large), 5, count=2048)
+    check_whole("f16", A, B, dict(outs, unsplit=unsplit, large=large))
     first = outs["ws S=1"]
     for k, v in outs.items():
         assert np.array_equal(v, first), k
@@ -389,7 +373,7 @@ def persistence(pg, mode):
 def test_persistent_matches_per_tile_kernel(pg, fmt, tile, M, N, K):
     # more tiles than the persistent grid holds, so workgroups stride over
     # several tiles (ragged edges in the last ones); same bits as the
-    # per-tile kernel, and inside the bound on sampled elements
+    # per-tile kernel, and inside the bound on every element
     kind = "f16_nt" if fmt == "f16" else "bf16_nt"
     A, B = inputs.make_operands(kind, M, N, K, 31 + M + K)
     dA, dB = dev_half(A, fmt), dev_half(B, fmt)
@@ -402,8 +386,8 @@ def test_persistent_matches_per_tile_kernel(pg, fmt, tile, M, N, K):
             with persistence(pg, 1):
                 ref_bits = run_nt(pg, fmt, "ws", A, B, S, dA, dB)
             assert np.array_equal(got, ref_bits), f"persistent S={S} differs from the per-tile kernel"
-    check_sampled(fmt, A, B, {"persistent": got}, 7, count=1024)
-    assert pg.pgemm_sync_status() == 0
+    check_whole(fmt, A, B, {"persistent": got})
+    assert pg.pgemm_debug_status() == 0
 
 
 def persistent_cases(n=16, seed=77):
@@ -432,7 +416,7 @@ def test_persistent_fuzzed_against_per_tile_kernel(pg, case):
         with persistence(pg, 1):
             want = run_nt(pg, fmt, "ws", A, B, S, dA, dB)
     assert np.array_equal(got, want)
-    assert pg.pgemm_sync_status() == 0
+    assert pg.pgemm_debug_status() == 0
 
 
 def test_persistent_k_zero(pg):
@@ -483,26 +467,26 @@ def test_missing_seed_times_out_instead_of_hanging(pg):
     # kernel still exits, and the host sees PGEMM_ERR_TIMEOUT.
     A, B = inputs.make_operands("f16_nt", 256, 128, 128, 9)
     dA, dB = dev_half(A, "f16"), dev_half(B, "f16")
-    assert pg.pgemm_sync_status() == 0
+    assert pg.pgemm_debug_status() == 0
     try:
         pg.pgemm_set_ws_debug(max_polls=2000, skip_seed=True)
         pg.pgemm_f16_nt_ws(dA, dB, stages=2)
-        assert pg.pgemm_sync_status() == 7  # PGEMM_ERR_TIMEOUT
+        assert pg.pgemm_debug_status() == 7  # PGEMM_ERR_TIMEOUT
     finally:
         pg.pgemm_set_ws_debug(0, False)
-    assert pg.pgemm_sync_status() == 0
+    assert pg.pgemm_debug_status() == 0
     got = run_nt(pg, "f16", "ws", A, B, 2, dA, dB)
     ref, mag = oracle.gemm_nt("f16", A, B)
     assert_within_bound("f16", got, ref, mag, "after reset")
-    assert pg.pgemm_sync_status() == 0
+    assert pg.pgemm_debug_status() == 0
     # the persistent kernel's waits are bounded the same way
     with tiling(pg, 128, 1), persistence(pg, 2):
         try:
             pg.pgemm_set_ws_debug(max_polls=2000, skip_seed=True)
             pg.pgemm_f16_nt_ws(dA, dB, stages=2)
-            assert pg.pgemm_sync_status() == 7
+            assert pg.pgemm_debug_status() == 7
         finally:
             pg.pgemm_set_ws_debug(0, False)
-        assert pg.pgemm_sync_status() == 0
+        assert pg.pgemm_debug_status() == 0
         got = run_nt(pg, "f16", "ws", A, B, 2, dA, dB)
     assert_within_bound("f16", got, ref, mag, "persistent, after reset")
