@@ -52,7 +52,9 @@ typedef enum {
   PGEMM_ERR_LDS = 5,     /* the tile ring for these stages exceeds LDS       */
   PGEMM_ERR_LAUNCH = 6,  /* the HIP launch (or a HIP query) failed           */
   PGEMM_ERR_TIMEOUT = 7, /* a credit wait exceeded its poll limit            */
-  PGEMM_ERR_DEVICE = 8   /* the current device is not gfx950                 */
+  PGEMM_ERR_DEVICE = 8,  /* the current device is not gfx950                 */
+  PGEMM_ERR_WORKSPACE = 9 /* pgemm_f16_nt_ws_static: the plan's K-split
+                            partial sums exceed the static scratch          */
 } pgemm_status;
 
 /* Variant codes used by the query functions. */
@@ -120,6 +122,24 @@ pgemm_status pgemm_f16_nt(const uint16_t *lhs, const uint16_t *rhs, uint16_t *ou
  */
 pgemm_status pgemm_f16_nt_ws(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out,
                              int64_t M, int64_t N, int64_t K, int stages, void *stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, plan, kernels and results as pgemm_f16_nt_ws, except that a
+ * K-split plan keeps its fp32 partial sums in a static scratch array that
+ * the library holds on each device it runs on (PGEMM_STATIC_SCRATCH_BYTES,
+ * until the process ends) instead of the stream's registered workspace; it
+ * never allocates, frees or waits.  Every split the planner chooses fits;
+ * a forced one (pgemm_set_tiling) needing more returns PGEMM_ERR_WORKSPACE
+ * before anything is enqueued.  All calls on one device share that scratch:
+ * calls that may run at the same time on one device (other streams, other
+ * host threads) race on it and must be serialised by the caller.  Nothing
+ * in it needs clearing: each call writes every partial sum it reads.
+ */
+#define PGEMM_STATIC_SCRATCH_BYTES (16ll << 20)
+pgemm_status pgemm_f16_nt_ws_static(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out,
+                                    int64_t M, int64_t N, int64_t K, int stages, void *stream);
 
 /* bfloat16 counterparts: bf16 operands, fp32 accumulation, bf16 output
  * rounded to nearest-even.  Same rules as the f16 calls. */

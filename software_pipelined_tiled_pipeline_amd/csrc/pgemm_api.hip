@@ -20,6 +20,16 @@
 // bit 0.  One copy per device; the host reaches it through its address.
 __device__ uint32_t pgemm_error_word;
 
+// Static K-split scratch of pgemm_f16_nt_ws_static: fp32 partial sums for
+// callers that cannot allocate.  Every split the planner chooses fits (a
+// split has at most 256 small tiles over all its pieces: split x tiles x
+// 128 x 128 floats = 16 MiB).  One copy per device, held until the process
+// ends.  Host code never uses this name as an address (on the host it is a
+// stand-in, not device memory): it uses g_scratch_ptr[dev], taken with
+// hipGetSymbolAddress when the library first meets the device.
+constexpr int64_t kStaticScratchBytes = PGEMM_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
 namespace {
 
 using namespace pgemm;
@@ -226,6 +236,7 @@ pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, int6
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 uint32_t *g_err_ptr[kMaxDevices];
+float *g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device
 std::mutex g_dev_mutex;
 
 pgemm_status current_device(int *dev_out) {
@@ -244,6 +255,9 @@ pgemm_status current_device(int *dev_out) {
         void *p = nullptr;
         if (hipGetSymbolAddress(&p, HIP_SYMBOL(pgemm_error_word)) != hipSuccess) return PGEMM_ERR_LAUNCH;
         g_err_ptr[dev] = static_cast<uint32_t *>(p);
+        void *sp = nullptr;
+        if (hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) != hipSuccess || !sp) return PGEMM_ERR_LAUNCH;
+        g_scratch_ptr[dev] = static_cast<float *>(sp);
       }
       g_dev_state[dev].store(st, std::memory_order_release);
     }
@@ -299,8 +313,11 @@ pgemm_status launch(Elem e, const NtLaunch &a, bool staged) {
   return staged ? launch_bf16_staged(a) : launch_bf16_direct(a);
 }
 
+// `use_static`: a split plan keeps its partial sums in the device's static
+// scratch (PGEMM_ERR_WORKSPACE if they do not fit) instead of the stream's
+// registered workspace.
 pgemm_status nt_entry(Elem e, pgemm_op op, const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int64_t M,
-                      int64_t N, int64_t K, int stages, void *stream) {
+                      int64_t N, int64_t K, int stages, void *stream, bool use_static = false) {
   pgemm_status st = check_ptrs(lhs, rhs, out, M, N, K);
   if (st != PGEMM_OK) return st;
   Plan p;
@@ -312,7 +329,10 @@ pgemm_status nt_entry(Elem e, pgemm_op op, const uint16_t *lhs, const uint16_t *
   if (st != PGEMM_OK) return st;
   std::unique_lock<std::mutex> lock;
   float *part = nullptr;
-  if (p.split > 1) {
+  if (p.split > 1 && use_static) {
+    if (p.info.workspace_bytes > kStaticScratchBytes) return PGEMM_ERR_WORKSPACE;
+    part = g_scratch_ptr[dev];
+  } else if (p.split > 1) {
     lock = std::unique_lock<std::mutex>(g_work_mutex);
     const Workspace *w = find_workspace(dev, stream);
     const int64_t avail = w ? w->bytes : 0;
@@ -384,6 +404,11 @@ pgemm_status pgemm_f16_nt(const uint16_t *lhs, const uint16_t *rhs, uint16_t *ou
 pgemm_status pgemm_f16_nt_ws(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int64_t M, int64_t N,
                              int64_t K, int stages, void *stream) {
   return nt_entry(Elem::F16, PGEMM_OP_NT_WS, lhs, rhs, out, M, N, K, stages, stream);
+}
+
+pgemm_status pgemm_f16_nt_ws_static(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int64_t M, int64_t N,
+                                    int64_t K, int stages, void *stream) {
+  return nt_entry(Elem::F16, PGEMM_OP_NT_WS, lhs, rhs, out, M, N, K, stages, stream, true);
 }
 
 pgemm_status pgemm_bf16_nt(const uint16_t *lhs, const uint16_t *rhs, uint16_t *out, int64_t M, int64_t N, int64_t K,
@@ -507,6 +532,7 @@ const char *pgemm_strerror(pgemm_status status) {
     case PGEMM_ERR_LAUNCH: return "HIP launch or query failed";
     case PGEMM_ERR_TIMEOUT: return "a credit wait exceeded its poll limit";
     case PGEMM_ERR_DEVICE: return "current device is not gfx950";
+    case PGEMM_ERR_WORKSPACE: return "the K-split partial sums exceed the static scratch (PGEMM_STATIC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

@@ -22,10 +22,11 @@ LIB_PATH = os.path.join(_HERE, "libpgemm.so")
 STATUS = {
     0: "PGEMM_OK", 1: "PGEMM_ERR_NULL", 2: "PGEMM_ERR_SHAPE", 3: "PGEMM_ERR_STAGES",
     4: "PGEMM_ERR_ALIGN", 5: "PGEMM_ERR_LDS", 6: "PGEMM_ERR_LAUNCH", 7: "PGEMM_ERR_TIMEOUT",
-    8: "PGEMM_ERR_DEVICE",
+    8: "PGEMM_ERR_DEVICE", 9: "PGEMM_ERR_WORKSPACE",
 }
 OPS = {"s32_nn": 0, "nt_swap": 1, "nt_ws": 2}
-GEMM_SYMBOLS = ("pgemm_s32_nn", "pgemm_f16_nt", "pgemm_f16_nt_ws", "pgemm_bf16_nt", "pgemm_bf16_nt_ws")
+GEMM_SYMBOLS = ("pgemm_s32_nn", "pgemm_f16_nt", "pgemm_f16_nt_ws", "pgemm_bf16_nt", "pgemm_bf16_nt_ws",
+                "pgemm_f16_nt_ws_static")
 
 
 class PgemmError(RuntimeError):
@@ -186,6 +187,17 @@ def _nt(name, dtype_name):
 
 pgemm_f16_nt = _nt("pgemm_f16_nt", "float16")
 pgemm_f16_nt_ws = _nt("pgemm_f16_nt_ws", "float16")
+
+
+def pgemm_f16_nt_ws_static(lhs, rhs, out=None, stages: int = 0, stream=None):
+    """pgemm_f16_nt_ws whose K-split partial sums live in the library's static
+    per-device scratch: the library allocates nothing (library call of the
+    same name).  Calls that may overlap on one device race on that scratch."""
+    import torch
+    out, M, N, K = _operands(lhs, rhs, out, torch.float16, nn=False)
+    return _call("pgemm_f16_nt_ws_static", lhs, rhs, out, M, N, K, stages, stream)
+
+
 pgemm_bf16_nt = _nt("pgemm_bf16_nt", "bfloat16")
 pgemm_bf16_nt_ws = _nt("pgemm_bf16_nt_ws", "bfloat16")
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_messages(L):
     assert pgemm.abi_version() == 3
-    for code in range(9):
+    for code in range(10):
         assert pgemm.strerror(code) and pgemm.strerror(code) != "unknown status"
     assert pgemm.strerror(99) == "unknown status"
 
