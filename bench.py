@@ -432,6 +432,8 @@ def main():
     ap.add_argument("--timed-only", action="store_true",
                     help="launch only the warm-up and timed steps of the chosen kernel (stages: --stages, else "
                          "the entry point's default), for profiling")
+    ap.add_argument("--tile", type=int, default=0, choices=[0, 128, 256],
+                    help="force the output tile of the NT workloads (pgemm_set_tiling; 0: planned)")
     ap.add_argument("--power", action="store_true",
                     help="after the timed region, sample board power over about 1 s of back-to-back steps")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
@@ -464,6 +466,8 @@ def main():
     from software_pipelined_tiled_pipeline_amd import inputs, pgemm
 
     pgemm.lib()  # fails loudly if the HIP library is missing
+    if args.tile:
+        pgemm.pgemm_set_tiling(args.tile, 0)
     if WORKLOADS[args.workload][4] == "s32":
         run_s32(args, torch, np)
         return
@@ -635,6 +639,7 @@ def main():
             "M": M, "N": N, "K": K,
             "variant": args.variant,
             "stages": stages,
+            "tile": pgemm.pgemm_query("nt_" + args.variant, stages, M, N, K)["block_m"],
             "pct_of_mfma_peak": round(100.0 * value / PEAK_F16_TFLOPS, 1),
             "stage_sweep_tflops": sweep,
             "single_launch_us": single_us,

@@ -14,9 +14,14 @@ using SwapGeom = NtGeom<256, 256, (S <= 2 ? 64 : 32), S, 2, 2, 0>;
 
 // Producer/consumer, large tile: 256 x 256 output tile, eight consumer waves
 // of 128 x 64 (two per SIMD) and four producer waves (one per SIMD), so
-// every wave is capped at 168 registers.  K tile 64 (64 KiB slots) for one
-// or two slots, 32 (32 KiB slots) for three or four, so that the ring and
-// the output staging tile fit in 160 KiB of LDS.
+// every wave is capped at 168 registers and a consumer holds one fragment
+// set.  K tile 64 (64 KiB slots) for one or two slots, 32 (32 KiB slots) for
+// three or four, so that the ring and the output staging tile fit in 160 KiB
+// of LDS.  (A 256 x 128 tile with four consumers and four producers, one of
+// each per SIMD, gives each wave 256 registers and the consumers two
+// fragment sets, but measured 10-20 % slower at 8192^3: a lone consumer per
+// SIMD idles it at every credit wait, and the narrower tile reads a third
+// more from L2 per flop.)
 template <int S>
 using WsGeom = NtGeom<256, 256, (S <= 2 ? 64 : 32), S, 2, 4, 4>;
 

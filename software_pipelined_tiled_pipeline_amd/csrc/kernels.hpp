@@ -276,6 +276,14 @@ struct StagedLoader {
     put(slot, j, fetch(t, j, p));
   }
 
+  // The largest batch of at most four instructions that divides `count`
+  // and is a whole number of parity periods.
+  static constexpr int batch(int count) {
+    for (int b = 4; b > 0; --b)
+      if (count % b == 0 && b % PAR == 0) return b;
+    return 0;
+  }
+
   // Instructions first .. first+COUNT-1 of the slot for tile t, in batches
   // of up to four granules: a batch's global loads, then its LDS writes
   // (four granules in flight bound the staging registers).
@@ -283,8 +291,8 @@ struct StagedLoader {
   __device__ __forceinline__ void load(char *slot, int t, int first, int lane) const {
     (void)lane;
     if (t >= nk) return;
-    constexpr int B = COUNT < 4 ? COUNT : 4;
-    static_assert(COUNT % B == 0 && B % PAR == 0, "batches keep the parity pattern");
+    constexpr int B = batch(COUNT);
+    static_assert(B > 0, "batches keep the parity pattern");
 #pragma unroll
     for (int b = 0; b < COUNT; b += B) {
       u32x4 v[B];
@@ -360,6 +368,14 @@ struct NtGeom {
   static constexpr int STAGE_BYTES = BM * Staging<BN>::PITCH;
   static constexpr int CTR_OFFSET = RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES;
   static constexpr int LDS_BYTES = CTR_OFFSET + (P > 0 ? 2 * S * 4 : 0);
+  // Registers per wave: a SIMD's 512 are shared evenly by the waves it holds
+  // (every wave of a kernel gets the same count, in steps of 8).
+  static constexpr int WAVES_PER_SIMD = (CW + P + 3) / 4;
+  static constexpr int REGS = (512 / WAVES_PER_SIMD) / 8 * 8;
+  // A consumer holds two fragment sets (reads the next k32 step during the
+  // current one) when its accumulators, both sets and about 28 registers
+  // of addresses and counters fit.
+  static constexpr bool TWO_SETS = WM / 16 * (WN / 16) * 4 + 2 * (WM / 16 + WN / 16) * 4 + 28 <= REGS;
   static_assert(Loader::INSTR % LOADERS == 0, "loads split evenly");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave blocks are whole 16x16 MFMA tiles");
   static_assert(S <= 4, "vmcnt wait table covers three tiles in flight");
@@ -523,6 +539,11 @@ __global__ void __launch_bounds__(G::THREADS)
                  int k_chunk, float *__restrict__ partial, int ldp, uint32_t max_polls, int skip_seed,
                  uint32_t *err) {
   static_assert(G::P > 0, "producer/consumer kernel needs producer waves");
+  // Arguments used only inside or after the K loop are read into SGPRs up
+  // front: a scalar load still in flight at the loop head (scalar loads
+  // return out of order) turns the first fragment wait of every tile into a
+  // wait for all outstanding LDS reads.
+  __asm__ volatile("" ::"s"(out), "s"(partial), "s"(ldp), "s"(err), "s"(max_polls));
   using Loader = std::conditional_t<STAGED, StagedLoader<G::BM, G::BN, G::BK>, typename G::Loader>;
   using Row = RingRow<G::BK>;
   constexpr int S = G::S, C = G::CW, P = G::P;
@@ -550,7 +571,7 @@ __global__ void __launch_bounds__(G::THREADS)
   // register budget (the 64 x 64 blocks of the 128 x 128 tile, not the
   // 128 x 64 ones of the large tile) read the next k32 step while the
   // current step's MFMAs run.
-  constexpr bool kTwoSets = (W::TM * W::TN + 2 * (W::TM + W::TN)) * 4 <= 144;
+  constexpr bool kTwoSets = G::TWO_SETS;
   if (wave < C) {
     // ---------------------------------------------------------- consumer
     if (!skip_seed)
@@ -559,13 +580,16 @@ __global__ void __launch_bounds__(G::THREADS)
     if constexpr (kTwoSets) {
       // The first step of tile t+1 is read during the last step of tile t,
       // so slot t is released as soon as its last reads have landed and
-      // `full` of tile t+1 is waited for before that last step.  Every tile
-      // runs the same code, the last one included (it reads the slot after
-      // it: landed or never-written data that is no longer refilled and is
-      // never used): with a separate tail the compiler kept the accumulators
-      // in other registers there and copied them right before MFMAs, a
-      // hazard it cannot see through the inline asm.
-      static_assert(W::NK % 2 == 0, "fragment sets line up per tile");
+      // `full` of tile t+1 is waited for before that last step (its counter
+      // is read at the start of the tile, so that a credit that has already
+      // arrived costs no LDS round trip).  The fragment sets alternate per
+      // k32 step; with one step per K tile they alternate per tile, and the
+      // loop body covers two tiles.  Every tile runs the same code, the last
+      // one included (it reads the slot after it: landed or never-written
+      // data that is no longer refilled and is never used): with a separate
+      // tail the compiler kept the accumulators in other registers there and
+      // copied them right before MFMAs, a hazard it cannot see through the
+      // inline asm.
       constexpr int NK = W::NK;
       const int r = W::lane_row(lane), chunk = W::lane_chunk(lane), sw = Row::swz(r);
       auto lane_a = [&](int s) { return slot_ptr(s) + (wm * G::WM + r) * Row::ROW_BYTES; };
@@ -576,16 +600,32 @@ __global__ void __launch_bounds__(G::THREADS)
         credit_wait(&full[0], (uint32_t)P, max_polls, err);
         W::read_frags(f[0], lane_a(0), lane_b(0), 0, chunk, sw);
       }
-      for (int t = 0; t < n_k; ++t) {
+      // tile t, whose first step runs on f[F0]
+      auto tile = [&](int t, auto f0) __attribute__((always_inline)) {
+        constexpr int F0 = decltype(f0)::value;
         const int s = t % S, s1 = (t + 1) % S;
+        const uint32_t next = credit_load(&full[s1]);
 #pragma unroll
         for (int kk = 0; kk + 1 < NK; ++kk)
-          w.template mixed_step<true, 0>(f[kk & 1], f[(kk + 1) & 1], lane_a(s), lane_b(s), kk + 1, chunk, sw,
-                                         no_load);
+          w.template mixed_step<true, 0>(f[(F0 + kk) & 1], f[(F0 + kk + 1) & 1], lane_a(s), lane_b(s), kk + 1,
+                                         chunk, sw, no_load);
         wait_lgkmcnt0();  // the last fragment reads of slot s are done
         credit_trigger(&empty[s]);
-        if (t + 1 < n_k) credit_wait(&full[s1], (uint32_t)P * ((uint32_t)((t + 1) / S) + 1u), max_polls, err);
-        w.template mixed_step<true, 0>(f[(NK - 1) & 1], f[NK & 1], lane_a(s1), lane_b(s1), 0, chunk, sw, no_load);
+        const uint32_t target = (uint32_t)P * ((uint32_t)((t + 1) / S) + 1u);
+        if (t + 1 < n_k && __builtin_amdgcn_readfirstlane(next) < target)
+          credit_wait(&full[s1], target, max_polls, err);
+        w.template mixed_step<true, 0>(f[(F0 + NK - 1) & 1], f[(F0 + NK) & 1], lane_a(s1), lane_b(s1), 0, chunk,
+                                       sw, no_load);
+      };
+      using C0 = std::integral_constant<int, 0>;
+      using C1 = std::integral_constant<int, 1>;
+      if constexpr (NK % 2 == 0) {
+        for (int t = 0; t < n_k; ++t) tile(t, C0{});
+      } else {
+        for (int t = 0; t < n_k; t += 2) {
+          tile(t, C0{});
+          if (t + 1 < n_k) tile(t + 1, C1{});
+        }
       }
       w.settle();
     } else {
@@ -677,6 +717,7 @@ __global__ void __launch_bounds__(G::THREADS)
                             uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m,
                             uint32_t max_polls, int skip_seed, uint32_t *err) {
   static_assert(G::P > 0, "producer/consumer kernel needs producer waves");
+  __asm__ volatile("" ::"s"(out), "s"(err), "s"(max_polls));  // see nt_ws_kernel
   using Loader = typename G::Loader;
   using Row = RingRow<G::BK>;
   constexpr int S = G::S, C = G::CW, P = G::P;

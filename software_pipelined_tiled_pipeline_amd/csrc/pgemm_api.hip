@@ -47,9 +47,9 @@ std::atomic<int> g_skip_seed{0};
 
 // ------------------------------------------------------------- planning
 //
-// The plan of an NT call: tile size, ring slots and K split.  Large
-// (256 x 256) tiles when they alone nearly fill the chip, small (128 x 128)
-// ones otherwise; a product that even then leaves most CUs idle and has a
+// The plan of an NT call: tile size, ring slots and K split.  Large tiles
+// (256 x 256 single schedule, 256 x 128 producer/consumer) when they alone
+// nearly fill the chip, small (128 x 128) ones otherwise; a product that even then leaves most CUs idle and has a
 // long K is split along K into pieces whose fp32 partial tiles a second
 // kernel adds up.  pgemm_set_tiling can force either choice.
 
@@ -150,10 +150,10 @@ int64_t split_workspace_bytes(int split, int64_t M, int64_t N) {
 
 // `avail`: bytes of workspace the call can use for a K split's partial sums;
 // a split that would need more is not planned.
-void choose_tiling(Plan *p, int64_t M, int64_t N, int64_t K, int64_t avail) {
+void choose_tiling(Plan *p, int64_t M, int64_t N, int64_t K, int64_t avail, bool ws) {
   const int force_tile = g_force_tile.load(std::memory_order_relaxed);
   const int force_split = g_force_split.load(std::memory_order_relaxed);
-  const int64_t large = cdiv(M, kLargeTile) * cdiv(N, kLargeTile);
+  const int64_t large = cdiv(M, kLargeTile) * cdiv(N, ws ? WsGeom<1>::BN : SwapGeom<1>::BN);
   p->tile = force_tile ? force_tile : (large >= kFillTiles ? kLargeTile : kSmallTile);
   int split = 1;
   if (p->tile == kSmallTile && K > 0) {
@@ -212,7 +212,7 @@ pgemm_status plan(pgemm_op op, int stages, int64_t M, int64_t N, int64_t K, int6
       const int s = stages == 0 ? (ws ? kWsDefaultStages : kSwapDefaultStages) : stages;
       if (s < 1 || s > (ws ? kWsMaxStages : kSwapMaxStages)) return PGEMM_ERR_STAGES;
       p->stages = s;
-      choose_tiling(p, M, N, K, avail);
+      choose_tiling(p, M, N, K, avail, ws);
       // the persistent kernel has the direct loader only
       if (ws && p->split == 1 && !p->staged) p->persistent = g_persist_mode.load(std::memory_order_relaxed) == 2;
       bool ok;
