@@ -210,7 +210,7 @@ def kernel_label(name):
     return name[:100]
 
 
-def summarize(dirs):
+def summarize(dirs, timed_steps=0):
     """Markdown tables from rocprofv3 CSV output: per kernel, the number of
     dispatches and their mean / min / max duration (kernel trace), and the
     mean over dispatches of each counter summed over its instances, with the
@@ -234,10 +234,15 @@ def summarize(dirs):
             for r in csv.DictReader(open(f)):
                 durs[short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
             lines.append(f"kernel trace `{os.path.relpath(f, d)}`\n")
-            lines.append("| kernel | dispatches | mean us | min us | max us |")
-            lines.append("|---|---|---|---|---|")
+            last = f" | mean of the last {timed_steps} us" if timed_steps else ""
+            lines.append(f"| kernel | dispatches | mean us | min us | max us{last} |")
+            lines.append("|---|---|---|---|---|" + ("---|" if timed_steps else ""))
             for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
-                lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+                row = f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f}"
+                if timed_steps:
+                    tail = v[-timed_steps:]
+                    row += f" | {sum(tail) / len(tail):.2f}"
+                lines.append(row + " |")
             lines.append("")
         for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
             per = defaultdict(float)
@@ -285,6 +290,56 @@ def summarize(dirs):
                 lines.append("| " + " | ".join(row) + " |")
             lines.append("")
     print("\n".join(lines))
+
+
+def _counter_per_dispatch(d, counter):
+    """[(kernel label, value summed over the counter's instances)] per
+    dispatch, in dispatch order, from the rocprofv3 CSV output under d."""
+    import csv
+    import glob
+    per, order = {}, []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = int(r["Dispatch_Id"])
+            if key not in per:
+                per[key] = [kernel_label(r["Kernel_Name"]), 0.0]
+                order.append(key)
+            per[key][1] += float(r["Counter_Value"])
+    return [tuple(per[k]) for k in sorted(order)]
+
+
+def reduce_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, args):
+    """HBM-side bytes per call of the timed kernel (and, for a K split, its
+    reduction) from FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), scaled
+    by what the same counters read for a plain 512 MiB device copy
+    (--calibrate-copy: 512 MiB read and 512 MiB written).  Prints the line
+    that recorded_traffic() reads back while the kernel sources are
+    unchanged."""
+    n = 512 << 20
+    cf = [v for k, v in _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE") if "copyBuffer" in k]
+    cw = [v for k, v in _counter_per_dispatch(copy_write_dir, "WRITE_SIZE") if "copyBuffer" in k]
+    read_scale = n / 1024 / (sum(cf) / len(cf))
+    write_scale = n / 1024 / (sum(cw) / len(cw))
+    M, N, K, _, fmt = WORKLOADS[args.workload]
+    kname = "nt_ws_kernel" if args.variant == "ws" else "nt_swap_kernel"
+
+    def per_call(d, counter):
+        rows = _counter_per_dispatch(d, counter)
+        main = [v for k, v in rows if k.startswith(kname + " ")][-args.steps:]
+        red = [v for k, v in rows if k.startswith("reduce_splits")][-args.steps:]
+        return (sum(main) + sum(red)) / len(main), len(main), len(red)
+
+    fetch, nf, nr = per_call(fetch_dir, "FETCH_SIZE")
+    write, _, _ = per_call(write_dir, "WRITE_SIZE")
+    rd, wr = fetch * 1024 * read_scale, write * 1024 * write_scale
+    alg = (M * K + N * K) * 2 + M * N * 2
+    print(f"# {args.workload} {kname} S={args.stages}: last {nf} calls{' (+ reduce_splits)' if nr else ''}; "
+          f"read scale {read_scale:.4f}, write scale {write_scale:.4f}")
+    print(f"#   FETCH_SIZE {fetch:.0f} KiB -> {rd:.4g} B read, WRITE_SIZE {write:.0f} KiB -> {wr:.4g} B written; "
+          f"algorithmic {alg} B; traffic / algorithmic {(rd + wr) / alg:.2f}")
+    print(f"traffic {kname} {args.workload} S={args.stages} src={kernel_source_hash()} bytes={int(rd + wr)}")
 
 
 def cpu_baseline(fmt, A, B, M, N, K, budget_s: float):
@@ -436,11 +491,19 @@ def main():
                     help="force the output tile of the NT workloads (pgemm_set_tiling; 0: planned)")
     ap.add_argument("--power", action="store_true",
                     help="after the timed region, sample board power over about 1 s of back-to-back steps")
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="HBM bytes per call of --workload/--variant/--stages (mean of the last --steps calls) "
+                         "from FETCH_SIZE / WRITE_SIZE runs and the --calibrate-copy runs; no GPU")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
-                    help="reduce rocprofv3 CSV output under DIR to markdown tables and exit (no GPU)")
+                    help="reduce rocprofv3 CSV output under DIR to markdown tables and exit (no GPU); with "
+                         "--steps, the trace table adds the mean of each kernel's last --steps dispatches "
+                         "(the timed steps of a --timed-only run)")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize)
+        summarize(args.summarize, args.steps if "--steps" in sys.argv else 0)
+        return
+    if args.traffic:
+        reduce_traffic(*args.traffic, args)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
