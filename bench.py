@@ -58,10 +58,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the sources that define the kernels' code (host planning and launch code
+# do not change what a kernel moves)
+KERNEL_SOURCES = ("device_common.hpp", "wave_mma.hpp", "kernels.hpp", "instances.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "software_pipelined_tiled_pipeline_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

@@ -51,31 +51,44 @@ inline bool validate(const std::vector<int> &stage, const std::vector<int> &orde
   return true;
 }
 
+// Stage and order of every statement that writes, and of every statement
+// that reads, one buffer.
+struct BufferUses {
+  struct Point {
+    int stage, order;
+  };
+  std::vector<Point> writes, reads;
+};
+
+inline BufferUses uses_of(int buffer, const std::vector<int> &stage, const std::vector<int> &order,
+                          const std::vector<Access> &acc) {
+  BufferUses u;
+  for (const Access &a : acc)
+    if (a.buffer == buffer) (a.write ? u.writes : u.reads).push_back({stage[a.stmt], order[a.stmt]});
+  return u;
+}
+
+// Copies of `buffer` the pipelined loop keeps.  A value written in stage d
+// and last read in stage u is alive across u - d iteration boundaries, so
+// u - d + 1 copies (the ring's slots); a buffer the loop never writes needs
+// its one copy.  One copy fewer suffices when no write reaches a read that
+// comes later in the body and in a later stage: then every read of an
+// iteration's value happens before the body writes the next one.
 inline int versions(int buffer, const std::vector<int> &stage, const std::vector<int> &order,
                     const std::vector<Access> &acc) {
-  int def = -1, use = -1;
-  for (const Access &a : acc) {
-    if (a.buffer != buffer) continue;
-    const int s = stage[a.stmt];
-    if (a.write)
-      def = def < 0 ? s : std::min(def, s);
-    else
-      use = std::max(use, s);
-  }
-  if (def < 0) return 1;
-  if (use < def) use = def;  // written, never read later: one version
-  int v = use - def + 1;
-  if (v >= 2) {
-    bool need = false;
-    for (const Access &w : acc) {
-      if (!w.write || w.buffer != buffer) continue;
-      for (const Access &r : acc)
-        if (!r.write && r.buffer == buffer && order[w.stmt] < order[r.stmt] && stage[w.stmt] < stage[r.stmt])
-          need = true;
-    }
-    if (!need) --v;
-  }
-  return v;
+  const BufferUses u = uses_of(buffer, stage, order, acc);
+  if (u.writes.empty()) return 1;
+  auto by_stage = [](const BufferUses::Point &x, const BufferUses::Point &y) { return x.stage < y.stage; };
+  const int first_write = std::min_element(u.writes.begin(), u.writes.end(), by_stage)->stage;
+  int last_read = first_write;  // a buffer written but not read later lives within its stage
+  if (!u.reads.empty()) last_read = std::max(last_read, std::max_element(u.reads.begin(), u.reads.end(), by_stage)->stage);
+  const int span = last_read - first_write + 1;
+  const bool carried = std::any_of(u.writes.begin(), u.writes.end(), [&](const BufferUses::Point &w) {
+    return std::any_of(u.reads.begin(), u.reads.end(), [&](const BufferUses::Point &r) {
+      return w.order < r.order && w.stage < r.stage;
+    });
+  });
+  return span >= 2 && !carried ? span - 1 : span;
 }
 
 struct Block {
