@@ -257,3 +257,25 @@ def test_split_calls_from_two_threads_on_one_stream(pg):
         for o in outs[i][1:]:
             assert np.array_equal(host_bits(o), first), f"thread {i}: a result differs"
     pg.release_workspace(s)
+
+
+# ------------------------------------------------ binding argument checks
+
+def test_binding_rejects_tensors_off_the_current_device(pg):
+    # host tensors (or tensors on another device) are refused in Python,
+    # before any pointer reaches the library
+    dA = torch.zeros((64, 32), dtype=torch.float16, device="cuda")
+    dB = torch.zeros((48, 32), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        pg.pgemm_f16_nt_ws(dA, dB, out=torch.zeros((64, 48), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        pg.pgemm_f16_nt(dA.cpu(), dB)
+    with pytest.raises(ValueError):
+        pg.pgemm_bf16_nt(dA.bfloat16(), dB.bfloat16().cpu())
+    with pytest.raises(ValueError):
+        pg.pgemm_f16_nt_ws_static(dA, dB, out=torch.zeros((64, 48), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        pg.pgemm_s32_nn(torch.zeros((4, 4), dtype=torch.int32), torch.zeros((4, 4), dtype=torch.int32, device="cuda"))
+    out = pg.pgemm_f16_nt_ws(dA, dB)  # the same call on device tensors runs
+    torch.cuda.synchronize()
+    assert out.is_cuda and torch.count_nonzero(out).item() == 0
