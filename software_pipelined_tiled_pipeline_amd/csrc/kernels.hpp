@@ -547,6 +547,12 @@ __global__ void __launch_bounds__(G::THREADS)
   using Loader = std::conditional_t<STAGED, StagedLoader<G::BM, G::BN, G::BK>, typename G::Loader>;
   using Row = RingRow<G::BK>;
   constexpr int S = G::S, C = G::CW, P = G::P;
+  // Each tile loaded whole by one producer (so one trigger of a slot's
+  // `full` per round), or shared by all producers (P triggers): shared when
+  // K is split or when a tile takes more loads than vmcnt can count (BK =
+  // 64); see the producer below.
+  constexpr bool kWholeTiles = !SPLIT && Loader::INSTR < 64;
+  constexpr int FP = kWholeTiles ? 1 : P;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint32_t *full = reinterpret_cast<uint32_t *>(smem + G::CTR_OFFSET);
   uint32_t *empty = full + S;
@@ -597,7 +603,7 @@ __global__ void __launch_bounds__(G::THREADS)
       typename W::Frags f[2];
       NoLoads no_load;
       if (n_k > 0) {
-        credit_wait(&full[0], (uint32_t)P, max_polls, err);
+        credit_wait(&full[0], (uint32_t)FP, max_polls, err);
         W::read_frags(f[0], lane_a(0), lane_b(0), 0, chunk, sw);
       }
       // tile t, whose first step runs on f[F0]
@@ -611,7 +617,7 @@ __global__ void __launch_bounds__(G::THREADS)
                                          chunk, sw, no_load);
         wait_lgkmcnt0();  // the last fragment reads of slot s are done
         credit_trigger(&empty[s]);
-        const uint32_t target = (uint32_t)P * ((uint32_t)((t + 1) / S) + 1u);
+        const uint32_t target = (uint32_t)FP * ((uint32_t)((t + 1) / S) + 1u);
         if (t + 1 < n_k && __builtin_amdgcn_readfirstlane(next) < target)
           credit_wait(&full[s1], target, max_polls, err);
         w.template mixed_step<true, 0>(f[(F0 + NK - 1) & 1], f[(F0 + NK) & 1], lane_a(s1), lane_b(s1), 0, chunk,
@@ -635,12 +641,12 @@ __global__ void __launch_bounds__(G::THREADS)
       uint32_t seen = 0;
       for (int t = 0; t < n_k; ++t) {
         const int s = t % S;
-        const uint32_t target = (uint32_t)P * ((uint32_t)(t / S) + 1u);
+        const uint32_t target = (uint32_t)FP * ((uint32_t)(t / S) + 1u);
         if (seen < target) credit_wait(&full[s], target, max_polls, err);
         compiler_fence();
         const uint32_t next = t + 1 < n_k ? credit_load(&full[(t + 1) % S]) : 0u;
         char *base = slot_ptr(s);
-        w.template mma_ktile<1>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES,
+        w.template mma_ktile<2>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES,
                                 lane);
         wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
         credit_trigger(&empty[s]);
@@ -652,39 +658,58 @@ __global__ void __launch_bounds__(G::THREADS)
     // ---------------------------------------------------------- producer
     Loader ld;
     ld.init(lhs, rhs, M, N, K, kb, klen, m0, n0, k_rotation<SPLIT>(bm, bn, n_k));
-    const int first = (wave - C) * G::PER_LOADER;
-    // The loads of tile t go straight into its slot (direct to LDS) once
-    // the slot's `empty` credit arrives; `full` of tile t is triggered after
-    // the loads of tile t + LAG are issued, when its own have landed.  LAG =
-    // S - 2 keeps the consumers fed: the tile they need next is complete
-    // once the producer holds the credit of the slot they just released.
-    // Staged loads have written the tile by the time the call returns, so
-    // `full` follows at once (LAG = 0), after the LDS writes complete.
-    constexpr int PER = G::PER_LOADER;
-    constexpr int LAG = (Loader::DIRECT && S >= 2) ? S - 2 : 0;
-    static_assert((LAG + 1) * PER < 64, "loads in flight fit the 6-bit vmcnt");
-    for (int t = 0; t < n_k; ++t) {
-      const int s = t % S;
-      credit_wait(&empty[s], (uint32_t)C * ((uint32_t)(t / S) + 1u), max_polls, err);
-      ld.template load<PER>(slot_ptr(s), t, first, lane);
-      if (t >= LAG) {
+    if constexpr (kWholeTiles) {
+      // Producer p loads tiles p, p + P, p + 2P, ... whole, each straight
+      // into its slot once the slot's `empty` credit arrives, and adds to
+      // `full` as soon as that tile has landed.  The producers take turns
+      // rather than all waking on the same credit and issuing their shares
+      // at once, and no `full` waits for a later tile's slot to come free.
+      for (int t = wave - C; t < n_k; t += P) {
+        const int s = t % S;
+        credit_wait(&empty[s], (uint32_t)C * ((uint32_t)(t / S) + 1u), max_polls, err);
+        ld.template load<Loader::INSTR>(slot_ptr(s), t, 0, lane);
         if constexpr (Loader::DIRECT)
-          wait_vmcnt<LAG * PER>();  // tile t - LAG landed
+          wait_vmcnt<0>();  // tile t landed
         else
           wait_lgkmcnt0();  // this wave's writes of tile t are done
-        credit_trigger(&full[(t - LAG) % S]);
+        credit_trigger(&full[s]);
       }
-    }
-    if constexpr (LAG >= 2) {
-      if (n_k >= 2) {
-        wait_vmcnt<PER>();
-        credit_trigger(&full[(n_k - 2) % S]);
+    } else {
+      // K split (skinny products, streamed from HBM) or BK = 64: every
+      // producer loads its share of every tile, so that each keeps LAG + 1
+      // tiles of loads in flight.  `full` of tile t is triggered after the loads of tile t
+      // + LAG are issued, when its own have landed.  LAG = S - 2 keeps the
+      // consumers fed: the tile they need next is complete once the
+      // producer holds the credit of the slot they just released.  Staged
+      // loads have written the tile by the time the call returns, so `full`
+      // follows at once (LAG = 0), after the LDS writes complete.
+      const int first = (wave - C) * G::PER_LOADER;
+      constexpr int PER = G::PER_LOADER;
+      constexpr int LAG = (Loader::DIRECT && S >= 2) ? S - 2 : 0;
+      static_assert((LAG + 1) * PER < 64, "loads in flight fit the 6-bit vmcnt");
+      for (int t = 0; t < n_k; ++t) {
+        const int s = t % S;
+        credit_wait(&empty[s], (uint32_t)C * ((uint32_t)(t / S) + 1u), max_polls, err);
+        ld.template load<PER>(slot_ptr(s), t, first, lane);
+        if (t >= LAG) {
+          if constexpr (Loader::DIRECT)
+            wait_vmcnt<LAG * PER>();  // tile t - LAG landed
+          else
+            wait_lgkmcnt0();  // this wave's writes of tile t are done
+          credit_trigger(&full[(t - LAG) % S]);
+        }
       }
-    }
-    if constexpr (LAG >= 1) {
-      if (n_k >= 1) {
-        wait_vmcnt<0>();
-        credit_trigger(&full[(n_k - 1) % S]);
+      if constexpr (LAG >= 2) {
+        if (n_k >= 2) {
+          wait_vmcnt<PER>();
+          credit_trigger(&full[(n_k - 2) % S]);
+        }
+      }
+      if constexpr (LAG >= 1) {
+        if (n_k >= 1) {
+          wait_vmcnt<0>();
+          credit_trigger(&full[(n_k - 1) % S]);
+        }
       }
     }
   }
@@ -765,9 +790,10 @@ __global__ void __launch_bounds__(G::THREADS)
     }
   } else {
     // ---------------------------------------------------------- producer
-    // As in nt_ws_kernel: loads direct to LDS once the slot's `empty` credit
-    // arrives, `full` of sequence entry g triggered LAG = S - 2 entries
-    // later, now across tile boundaries.
+    // As nt_ws_kernel does for a K split: every producer loads its share of
+    // each entry direct to LDS once the slot's `empty` credit arrives, and
+    // `full` of sequence entry g is triggered LAG = S - 2 entries later, now
+    // across tile boundaries.
     constexpr int PER = G::PER_LOADER;
     constexpr int LAG = S >= 2 ? S - 2 : 0;
     static_assert((LAG + 1) * PER < 64, "loads in flight fit the 6-bit vmcnt");

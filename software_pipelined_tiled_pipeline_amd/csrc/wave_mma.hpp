@@ -142,12 +142,14 @@ struct WaveTile {
   }
 
   // One K tile from a ring slot with a single fragment set: the rhs pieces
-  // of a k32 step first, then the lhs pieces, AHEAD (0 or 1) block rows
-  // before the MFMAs that use them.  a_rows / b_rows: LDS address of the
-  // first of this wave's lhs / rhs rows in the slot.
+  // of a k32 step first, then the lhs pieces, each AHEAD block rows before
+  // the MFMAs that use it (a ring of AHEAD + 1 lhs pieces).  a_rows /
+  // b_rows: LDS address of the first of this wave's lhs / rhs rows in the
+  // slot.
   template <int AHEAD>
   __device__ __forceinline__ void mma_ktile(const char *a_rows, const char *b_rows, int lane) {
-    static_assert(AHEAD == 0 || AHEAD == 1, "at most one lhs piece read ahead");
+    static_assert(AHEAD >= 0 && AHEAD < TM, "lhs pieces read ahead within the k32 step");
+    constexpr int NA = AHEAD + 1;
     const int r = lane_row(lane);
     const int chunk = lane_chunk(lane);
     const int s = Row::swz(r);
@@ -156,20 +158,17 @@ struct WaveTile {
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const int p = ((4 * kk + chunk) ^ s) * 16;
-      u32x4 b[TN], a[2];
+      u32x4 b[TN], a[NA];
 #pragma unroll
       for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const u32x4 *>(lane_b + 16 * j * Row::ROW_BYTES + p);
-      if constexpr (AHEAD) a[0] = *reinterpret_cast<const u32x4 *>(lane_a + p);
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) a[i] = *reinterpret_cast<const u32x4 *>(lane_a + 16 * i * Row::ROW_BYTES + p);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        if constexpr (AHEAD) {
-          if (i + 1 < TM)
-            a[(i + 1) & 1] = *reinterpret_cast<const u32x4 *>(lane_a + 16 * (i + 1) * Row::ROW_BYTES + p);
-        } else {
-          a[i & 1] = *reinterpret_cast<const u32x4 *>(lane_a + 16 * i * Row::ROW_BYTES + p);
-        }
+        if (i + AHEAD < TM)
+          a[(i + AHEAD) % NA] = *reinterpret_cast<const u32x4 *>(lane_a + 16 * (i + AHEAD) * Row::ROW_BYTES + p);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) Mfma<T>::template run<ACC_AGPR>(b[j], a[i & 1], acc[i][j]);
+        for (int j = 0; j < TN; ++j) Mfma<T>::template run<ACC_AGPR>(b[j], a[i % NA], acc[i][j]);
       }
     }
   }

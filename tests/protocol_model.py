@@ -67,13 +67,22 @@ class Result:
 def ws_programs(S: int, n_k: int, P: int, C: int, *, bootstrap: bool = True, early_release: bool = False,
                 producer_trips: Optional[int] = None, consumer_trips: Optional[int] = None,
                 lookahead: int = 0, no_sync: bool = False, lag: Optional[int] = None,
-                read_after_last: bool = False):
-    """Producer/consumer: P producers (share p of every slot), C consumers.
+                read_after_last: bool = False, whole_tiles: bool = False, full_per_round: Optional[int] = None,
+                publish_before_landing: bool = False):
+    """Producer/consumer: P producers, C consumers.
 
-    As in the kernel, a producer issues its share of tile t as an
-    asynchronous load once slot t mod S has its `empty` credit, and adds to
-    `full` of tile t - lag after waiting for that tile's loads (lag = S - 2,
-    at least 0); the last `lag` tiles are completed after the loop.
+    Shared tiles (whole_tiles=False; the kernel's K-split form): producer p
+    issues its share of tile t as an asynchronous load once slot t mod S has
+    its `empty` credit, and adds to `full` of tile t - lag after waiting for
+    that tile's loads (lag = S - 2, at least 0); the last `lag` tiles are
+    completed after the loop.  Consumers wait for P additions per round.
+
+    Whole tiles (whole_tiles=True; the kernel's unsplit form): producer p
+    loads tiles p, p + P, ... whole, each once its slot has its `empty`
+    credit, and adds to `full` once that tile has landed.  Consumers wait
+    for one addition per round (full_per_round overrides the count they
+    wait for; publish_before_landing adds to `full` before the wait for the
+    loads: both planted mistakes).
 
     Faults: bootstrap=False drops the consumers' initial `empty` credits;
     early_release adds to `empty` before the slot's reads finish; *_trips
@@ -85,6 +94,26 @@ def ws_programs(S: int, n_k: int, P: int, C: int, *, bootstrap: bool = True, ear
     ct = n_k if consumer_trips is None else consumer_trips
     lg = max(S - 2, 0) if lag is None else lag
     progs = []
+    if whole_tiles:
+        for p in range(P):
+            prog = []
+            for t in range(p, pt, P):
+                s, r = t % S, t // S
+                if not no_sync:
+                    prog.append((WAIT, "empty", s, C * (r + 1 - lookahead)))
+                prog.append((ISSUE, s, t, 0))
+                if not no_sync:
+                    if publish_before_landing:
+                        prog.append((ADD, "full", s))
+                        prog.append((WAITLOADS, t))
+                    else:
+                        prog.append((WAITLOADS, t))
+                        prog.append((ADD, "full", s))
+            prog.append((WAITLOADS, 10 ** 9))
+            progs.append(prog)
+        fp = 1 if full_per_round is None else full_per_round
+        progs += _consumers(S, ct, C, fp, bootstrap, no_sync, early_release, read_after_last)
+        return progs, 1  # one share per slot: the whole tile
     for p in range(P):
         prog = []
         for t in range(pt):
@@ -101,6 +130,15 @@ def ws_programs(S: int, n_k: int, P: int, C: int, *, bootstrap: bool = True, ear
                 prog.append((ADD, "full", t % S))
         prog.append((WAITLOADS, 10 ** 9))
         progs.append(prog)
+    progs += _consumers(S, ct, C, P if full_per_round is None else full_per_round, bootstrap, no_sync,
+                        early_release, read_after_last)
+    return progs, P  # shares per slot: one per producer
+
+
+def _consumers(S, ct, C, fp, bootstrap, no_sync, early_release, read_after_last):
+    """C consumers: seed every slot's `empty`, then per tile wait for fp
+    additions to `full` per round, read the slot, release it."""
+    progs = []
     for c in range(C):
         prog = []
         if bootstrap and not no_sync:
@@ -109,7 +147,7 @@ def ws_programs(S: int, n_k: int, P: int, C: int, *, bootstrap: bool = True, ear
         for t in range(ct):
             s, r = t % S, t // S
             if not no_sync:
-                prog.append((WAIT, "full", s, P * (r + 1)))
+                prog.append((WAIT, "full", s, fp * (r + 1)))
             if early_release and not no_sync:
                 prog.append((ADD, "empty", s))
             prog.append((RBEGIN, s, t))
@@ -120,7 +158,7 @@ def ws_programs(S: int, n_k: int, P: int, C: int, *, bootstrap: bool = True, ear
             prog.append((RBEGIN, ct % S, None))
             prog.append((REND, ct % S, None))
         progs.append(prog)
-    return progs, P  # shares per slot: one per producer
+    return progs
 
 
 def swap_programs(S: int, n_k: int, W: int, *, skip_barrier: bool = False, skip_wait: bool = False,

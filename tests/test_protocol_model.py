@@ -188,3 +188,56 @@ def test_refill_before_the_barrier_is_caught(S):
     # reading tile t: the copy may land in the buffer still being read
     r = check_swap(S, S + 1, 2, refill_before_barrier=True, stop_at_first=True)
     assert r.raw or r.war
+
+
+# ------------------------------------------- whole tiles, one producer each
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("n_k", [0, 1, 2, 3, 5, 6])
+@pytest.mark.parametrize("P,C", [(1, 1), (2, 1), (2, 2), (3, 1)])
+def test_ws_whole_tiles_safe_in_every_interleaving(S, n_k, P, C):
+    # producer p loads tiles p, p + P, ... whole and publishes each once it
+    # has landed; consumers wait for one addition to `full` per round
+    if P * C >= 4 and n_k >= 5 and S >= 3:
+        pytest.skip("covered by the random walks below")
+    r = check_ws(S, n_k, P, C, whole_tiles=True)
+    assert r.ok, r.example
+    r = check_ws(S, n_k, P, C, whole_tiles=True, read_after_last=True)
+    assert r.ok, r.example
+
+
+@pytest.mark.parametrize("S,n_k,P,C", [(4, 16, 4, 8), (3, 12, 4, 8), (4, 9, 2, 4), (3, 10, 2, 4), (1, 8, 4, 8)])
+def test_ws_whole_tiles_safe_on_random_interleavings(S, n_k, P, C):
+    # the kernels' role counts (4 producers / 8 consumers, 2 / 4), with more
+    # producers than slots as well (S = 3, 1)
+    r = check_ws(S, n_k, P, C, whole_tiles=True, exhaustive=False, walks=200, seed=S * 7 + n_k)
+    assert r.ok, r.example
+    r = check_ws(S, n_k, P, C, whole_tiles=True, read_after_last=True, exhaustive=False, walks=100, seed=n_k)
+    assert r.ok, r.example
+
+
+def test_whole_tiles_waiting_for_every_producer_deadlocks():
+    # consumers that still wait for P additions per round never see them
+    r = check_ws(2, 3, 2, 1, whole_tiles=True, full_per_round=2, stop_at_first=True)
+    assert r.deadlock, r.example
+
+
+def test_whole_tiles_published_before_landing_is_caught():
+    r = check_ws(2, 3, 2, 1, whole_tiles=True, publish_before_landing=True, stop_at_first=True)
+    assert r.raw, r.example
+
+
+def test_kernel_whole_tile_producer_matches_the_model():
+    # the unsplit nt_ws_kernel's producer: tiles p, p + P, ... whole, wait
+    # for the slot's `empty`, load, wait for every load of the tile, then
+    # one addition to `full`; consumers wait for one addition per round
+    src = open(KERNELS).read()
+    body = src[src.index("if constexpr (kWholeTiles) {"):src.index("} else {", src.index("if constexpr (kWholeTiles) {"))]
+    loop = body.index("for (int t = wave - C; t < n_k; t += P) {")
+    wait = body.index("credit_wait(&empty[s], (uint32_t)C * ((uint32_t)(t / S) + 1u)", loop)
+    load = body.index("ld.template load<Loader::INSTR>(slot_ptr(s), t, 0, lane);", wait)
+    landed = body.index("wait_vmcnt<0>();  // tile t landed", load)
+    publish = body.index("credit_trigger(&full[s]);", landed)
+    assert loop < wait < load < landed < publish
+    assert "constexpr int FP = kWholeTiles ? 1 : P;" in src
+    assert "constexpr bool kWholeTiles = !SPLIT && Loader::INSTR < 64;" in src
