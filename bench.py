@@ -65,12 +65,20 @@ def log(*a):
 KERNEL_SOURCES = ("device_common.hpp", "wave_mma.hpp", "kernels.hpp", "instances.hpp")
 
 
-def kernel_source_hash() -> str:
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines, each line stripped: what
+    the compiler sees, so that a comment edit keeps a recorded hash."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", line).strip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
+def kernel_source_hash(csrc=None) -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "software_pipelined_tiled_pipeline_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "software_pipelined_tiled_pipeline_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -677,12 +677,12 @@ __global__ void __launch_bounds__(G::THREADS)
     } else {
       // K split (skinny products, streamed from HBM) or BK = 64: every
       // producer loads its share of every tile, so that each keeps LAG + 1
-      // tiles of loads in flight.  `full` of tile t is triggered after the loads of tile t
-      // + LAG are issued, when its own have landed.  LAG = S - 2 keeps the
-      // consumers fed: the tile they need next is complete once the
-      // producer holds the credit of the slot they just released.  Staged
-      // loads have written the tile by the time the call returns, so `full`
-      // follows at once (LAG = 0), after the LDS writes complete.
+      // tiles of loads in flight.  `full` of tile t is triggered after the
+      // loads of tile t + LAG are issued, when its own have landed.  LAG =
+      // S - 2 keeps the consumers fed: the tile they need next is complete
+      // once the producer holds the credit of the slot they just released.
+      // Staged loads have written the tile by the time the call returns, so
+      // `full` follows at once (LAG = 0), after the LDS writes complete.
       const int first = (wave - C) * G::PER_LOADER;
       constexpr int PER = G::PER_LOADER;
       constexpr int LAG = (Loader::DIRECT && S >= 2) ? S - 2 : 0;

@@ -68,3 +68,21 @@ def test_ragged_workload_line():
     ref = j["reference_library"]
     assert ref["call"].startswith("torch.mm") and ref["tflops"] > 0
 
+
+
+def test_kernel_hash_ignores_comments_only(tmp_path):
+    # the traffic record stays valid across comment edits, not code edits
+    sys.path.insert(0, ROOT)
+    import bench
+    csrc = os.path.join(ROOT, "software_pipelined_tiled_pipeline_amd", "csrc")
+    for name in bench.KERNEL_SOURCES:
+        (tmp_path / name).write_text(open(os.path.join(csrc, name), encoding="utf-8").read(), encoding="utf-8")
+    base = bench.kernel_source_hash(str(tmp_path))
+    assert base == bench.kernel_source_hash()
+    k = tmp_path / "kernels.hpp"
+    text = k.read_text(encoding="utf-8")
+    k.write_text("// a new comment\n\n" + text.replace("\n", "  // trailing\n", 3) + "\n/* block\n comment */\n",
+                 encoding="utf-8")
+    assert bench.kernel_source_hash(str(tmp_path)) == base
+    k.write_text(text + "\nconstexpr int kCodeChange = 1;\n", encoding="utf-8")
+    assert bench.kernel_source_hash(str(tmp_path)) != base
