@@ -746,6 +746,10 @@ __global__ void __launch_bounds__(G::THREADS)
   using Loader = typename G::Loader;
   using Row = RingRow<G::BK>;
   constexpr int S = G::S, C = G::CW, P = G::P;
+  // whole entries by one producer, or shared by all of them (BK = 64), as
+  // in nt_ws_kernel
+  constexpr bool kWholeTiles = Loader::INSTR < 64;
+  constexpr int FP = kWholeTiles ? 1 : P;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint32_t *full = reinterpret_cast<uint32_t *>(smem + G::CTR_OFFSET);
   uint32_t *empty = full + S;
@@ -771,60 +775,91 @@ __global__ void __launch_bounds__(G::THREADS)
     const int wm = wave / G::WGN, wn = wave % G::WGN;
     if (!skip_seed)
       for (int s = 0; s < S; ++s) credit_trigger(&empty[s]);  // every slot starts free
-    uint32_t g = 0;  // position in the workgroup's (tile, K tile) sequence
+    // `full` of the next entry's slot is read at the start of each entry and
+    // checked after its MFMAs, as in nt_ws_kernel
+    const uint32_t total = (uint32_t)my_tiles * (uint32_t)n_k;
+    uint32_t g = 0, seen = 0;  // position in the workgroup's (tile, K tile) sequence
     for (int it = 0; it < my_tiles; ++it) {
       int bm, bn;
       tile_of(it, &bm, &bn);
       w.zero();
       for (int t = 0; t < n_k; ++t, ++g) {
         const int s = (int)(g % S);
-        credit_wait(&full[s], (uint32_t)P * (g / S + 1u), max_polls, err);
+        const uint32_t target = (uint32_t)FP * (g / S + 1u);
+        if (seen < target) credit_wait(&full[s], target, max_polls, err);
+        compiler_fence();
+        const uint32_t next = g + 1 < total ? credit_load(&full[(g + 1) % S]) : 0u;
         char *base = slot_ptr(s);
-        w.template mma_ktile<0>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES,
-                                lane);
+        w.template mma_ktile<(G::WM > 64 ? 2 : 1)>(base + wm * G::WM * Row::ROW_BYTES,
+                                                    base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
         wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
         credit_trigger(&empty[s]);
+        seen = __builtin_amdgcn_readfirstlane(next);
       }
       w.settle();
       w.store_direct(out, M, N, bm * G::BM + wm * G::WM, bn * G::BN + wn * G::WN, lane);
     }
   } else {
     // ---------------------------------------------------------- producer
-    // As nt_ws_kernel does for a K split: every producer loads its share of
-    // each entry direct to LDS once the slot's `empty` credit arrives, and
-    // `full` of sequence entry g is triggered LAG = S - 2 entries later, now
-    // across tile boundaries.
-    constexpr int PER = G::PER_LOADER;
-    constexpr int LAG = S >= 2 ? S - 2 : 0;
-    static_assert((LAG + 1) * PER < 64, "loads in flight fit the 6-bit vmcnt");
-    const int first = (wave - C) * PER;
-    Loader ld;
-    uint32_t g = 0;
-    for (int it = 0; it < my_tiles; ++it) {
-      int bm, bn;
-      tile_of(it, &bm, &bn);
-      ld.init(lhs, rhs, M, N, K, 0, K, bm * G::BM, bn * G::BN);
-      for (int t = 0; t < n_k; ++t, ++g) {
+    const uint32_t total = (uint32_t)my_tiles * (uint32_t)n_k;
+    if constexpr (kWholeTiles) {
+      // As in nt_ws_kernel: producer p loads entries p, p + P, ... of the
+      // sequence whole, direct to LDS once the slot's `empty` credit
+      // arrives, and adds to `full` once the entry has landed, now across
+      // tile boundaries.
+      Loader ld;
+      int cur = -1;
+      for (uint32_t g = (uint32_t)(wave - C); g < total; g += P) {
+        const int it = (int)(g / (uint32_t)n_k), t = (int)(g - (uint32_t)it * (uint32_t)n_k);
+        if (it != cur) {
+          int bm, bn;
+          tile_of(it, &bm, &bn);
+          ld.init(lhs, rhs, M, N, K, 0, K, bm * G::BM, bn * G::BN);
+          cur = it;
+        }
         const int s = (int)(g % S);
         credit_wait(&empty[s], (uint32_t)C * (g / S + 1u), max_polls, err);
-        ld.template load<PER>(slot_ptr(s), t, first, lane);
-        if (g >= (uint32_t)LAG) {
-          wait_vmcnt<LAG * PER>();  // entry g - LAG landed
-          credit_trigger(&full[(g - LAG) % S]);
+        ld.template load<Loader::INSTR>(slot_ptr(s), t, 0, lane);
+        wait_vmcnt<0>();  // entry g landed
+        credit_trigger(&full[s]);
+      }
+    } else {
+      // BK = 64: every producer loads its share of each entry, and `full`
+      // of entry g is triggered LAG = S - 2 entries later, as nt_ws_kernel
+      // does for its shared tiles.
+      constexpr int PER = G::PER_LOADER;
+      constexpr int LAG = S >= 2 ? S - 2 : 0;
+      static_assert((LAG + 1) * PER < 64, "loads in flight fit the 6-bit vmcnt");
+      const int first = (wave - C) * PER;
+      Loader ld;
+      uint32_t g = 0;
+      for (int it = 0; it < my_tiles; ++it) {
+        int bm, bn;
+        tile_of(it, &bm, &bn);
+        ld.init(lhs, rhs, M, N, K, 0, K, bm * G::BM, bn * G::BN);
+        for (int t = 0; t < n_k; ++t, ++g) {
+          const int s = (int)(g % S);
+          credit_wait(&empty[s], (uint32_t)C * (g / S + 1u), max_polls, err);
+          ld.template load<PER>(slot_ptr(s), t, first, lane);
+          if (g >= (uint32_t)LAG) {
+            wait_vmcnt<LAG * PER>();  // entry g - LAG landed
+            credit_trigger(&full[(g - LAG) % S]);
+          }
         }
       }
-    }
-    if constexpr (LAG >= 2) {
-      if (g >= 2) {
-        wait_vmcnt<PER>();
-        credit_trigger(&full[(g - 2) % S]);
+      if constexpr (LAG >= 2) {
+        if (g >= 2) {
+          wait_vmcnt<PER>();
+          credit_trigger(&full[(g - 2) % S]);
+        }
       }
-    }
-    if constexpr (LAG >= 1) {
-      if (g >= 1) {
-        wait_vmcnt<0>();
-        credit_trigger(&full[(g - 1) % S]);
+      if constexpr (LAG >= 1) {
+        if (g >= 1) {
+          wait_vmcnt<0>();
+          credit_trigger(&full[(g - 1) % S]);
+        }
       }
+      (void)total;
     }
   }
 }
