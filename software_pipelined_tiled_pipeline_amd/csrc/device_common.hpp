@@ -34,15 +34,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 
 // One wave-wide direct-to-LDS load: lane l copies 16 bytes from
-// rsrc + voffset(l) + soffset to lds_dst + 16 * l.  `lds_dst` and `soffset`
-// must be wave-uniform.  Out-of-range reads return zero.  Callers keep the
-// row part of an offset in voffset and only the K offset in soffset, and
-// send a lane whose chunk lies past K to kOobOffset: then a lane reads zero
-// exactly when its element is outside the matrix, whether or not the
-// hardware adds soffset before the bound check.
-__device__ __forceinline__ void load_lds_x4(__amdgpu_buffer_rsrc_t rsrc, char *lds_dst, uint32_t voffset,
-                                            uint32_t soffset = 0) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds_dst, 16, voffset, soffset, 0, 0);
+// rsrc + voffset(l) + soffset to lds_base + 1024 G + 16 * l.  `lds_base` and
+// `soffset` must be wave-uniform.  Out-of-range reads return zero.  Callers
+// keep the row part of an offset in voffset and only the K offset in
+// soffset, and send a lane whose chunk lies past K to kOobOffset: then a
+// lane reads zero exactly when its element is outside the matrix, whether or
+// not the hardware adds soffset before the bound check.
+//
+// The LDS destination is held in M0.  Writing M0 while an earlier
+// direct-to-LDS load is still being issued stalls the wave (on gfx950 an
+// MFMA stream with one such load every 4 to 8 MFMAs lost 17-26 cycles per
+// load when each load set M0, 2-9 when they shared one value), so up to four
+// consecutive 1 KiB destinations are reached from one base through the
+// instruction offset (G KiB, at most 4095 bytes).  That offset is added to
+// the global address too, so voffset is lowered by as much: the 32-bit sum
+// wraps (checked on the device), and a lane sent to kOobOffset stays out of
+// range.  Loads that pass the same lds_base share M0.
+template <int G>
+__device__ __forceinline__ void load_lds_x4(__amdgpu_buffer_rsrc_t rsrc, char *lds_base, uint32_t voffset,
+                                            uint32_t soffset) {
+  static_assert(G >= 0 && G < 4, "the instruction offset holds at most 4095 bytes");
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds_base, 16, voffset - 1024u * G, soffset, 1024 * G, 0);
 }
 
 // s_waitcnt through the builtin, so that the compiler's own wait insertion

@@ -159,12 +159,15 @@ struct SlotLoader {
     }
   }
 
-  // Instruction j of the slot for the t-th K tile of the sequence (lane l ->
-  // granule 64 j + l); p = j mod PAR, passed as a constant (every caller's
-  // first instruction is a multiple of PAR, as is A_INSTR) so that the
-  // per-lane arrays stay in registers.  The t-th tile is K tile
+  // Instruction j = first + i of the slot for the t-th K tile of the sequence
+  // (lane l -> granule 64 j + l); p = j mod PAR, passed as a constant (every
+  // caller's first instruction is a multiple of PAR, as is A_INSTR) so that
+  // the per-lane arrays stay in registers.  `first` is a multiple of 4 and i
+  // a constant after unrolling, so instructions first + 4q .. first + 4q + 3
+  // share one LDS base (one M0 value).  The t-th tile is K tile
   // (t + rot) mod nk; t >= nk (issued past the end) stays out of range.
-  __device__ __forceinline__ void load_one(char *slot, int t, int j, int p) const {
+  __device__ __forceinline__ void load_one(char *slot, int t, int first, int i, int p) const {
+    const int j = first + i;
     const bool is_a = j < A_INSTR;
     const int jj = is_a ? j : j - A_INSTR;
     int kt = t;
@@ -175,7 +178,14 @@ struct SlotLoader {
     const int k0 = kt * BK;
     uint32_t voff = lane_off[p] + (uint32_t)(jj * RPI) * (uint32_t)pitch * 2u;
     if (lane_k[p] >= klen - k0) voff = kOobOffset;  // chunk past K (every lane, past the last tile)
-    load_lds_x4(is_a ? ra : rb, slot + j * (kWave * 16), voff, (uint32_t)k0 * 2u);
+    char *base = slot + (first + (i & ~3)) * (kWave * 16);
+    const __amdgpu_buffer_rsrc_t rs = is_a ? ra : rb;
+    switch (i & 3) {
+      case 0: load_lds_x4<0>(rs, base, voff, (uint32_t)k0 * 2u); break;
+      case 1: load_lds_x4<1>(rs, base, voff, (uint32_t)k0 * 2u); break;
+      case 2: load_lds_x4<2>(rs, base, voff, (uint32_t)k0 * 2u); break;
+      default: load_lds_x4<3>(rs, base, voff, (uint32_t)k0 * 2u); break;
+    }
   }
 
   // Instructions first .. first+COUNT-1 of the slot for tile t.
@@ -183,7 +193,7 @@ struct SlotLoader {
   __device__ __forceinline__ void load(char *slot, int t, int first, int lane) const {
     (void)lane;
 #pragma unroll
-    for (int i = 0; i < COUNT; ++i) load_one(slot, t, first + i, i % PAR);
+    for (int i = 0; i < COUNT; ++i) load_one(slot, t, first, i, i % PAR);
   }
 };
 
@@ -311,7 +321,7 @@ struct RefillLoads {
   Loader ld;
   char *slot;
   int tile, first;
-  __device__ __forceinline__ void operator()(int i) const { ld.load_one(slot, tile, first + i, i % Loader::PAR); }
+  __device__ __forceinline__ void operator()(int i) const { ld.load_one(slot, tile, first, i, i % Loader::PAR); }
 };
 struct NoLoads {
   __device__ __forceinline__ void operator()(int) const {}
@@ -377,6 +387,7 @@ struct NtGeom {
   // of addresses and counters fit.
   static constexpr bool TWO_SETS = WM / 16 * (WN / 16) * 4 + 2 * (WM / 16 + WN / 16) * 4 + 28 <= REGS;
   static_assert(Loader::INSTR % LOADERS == 0, "loads split evenly");
+  static_assert(PER_LOADER % 4 == 0, "every loader's first instruction starts a group of four (one M0 value)");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave blocks are whole 16x16 MFMA tiles");
   static_assert(S <= 4, "vmcnt wait table covers three tiles in flight");
   static_assert(P > 0 || S * PER_LOADER < 64, "in-flight loads fit the 6-bit vmcnt");
