@@ -86,3 +86,91 @@ def test_kernel_hash_ignores_comments_only(tmp_path):
     assert bench.kernel_source_hash(str(tmp_path)) == base
     k.write_text(text + "\nconstexpr int kCodeChange = 1;\n", encoding="utf-8")
     assert bench.kernel_source_hash(str(tmp_path)) != base
+
+
+# ------------------------------------------------------------------------
+# The reductions that turn rocprofv3 CSV output into the tables and the
+# traffic record under profiles/, on small synthetic files whose expected
+# figures are worked out by hand.
+
+WS_NAME = "_ZN5pgemm12nt_ws_kernelIDF16_NS_6NtGeomILi256ELi256ELi32ELi4ELi2ELi4ELi4ELi1EEELb0ELb0EEEvPKtS4_PtiiiiiiiPfijiPj"
+SPLIT_NAME = "_ZN5pgemm12nt_ws_kernelIDF16_NS_6NtGeomILi128ELi128ELi64ELi3ELi2ELi2ELi2ELi1EEELb1ELb0EEEvPKtS4_PtiiiiiiiPfijiPj"
+RED_NAME = "_ZN5pgemm13reduce_splitsIDF16_EEvPKfPtiiii"
+COPY_NAME = "__amd_rocclr_copyBuffer"
+
+
+def write_trace(d, rows):
+    """rows: (kernel name, start ns, end ns)"""
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_kernel_trace.csv"), "w") as f:
+        f.write('"Kind","Dispatch_Id","Kernel_Name","Start_Timestamp","End_Timestamp"\n')
+        for i, (name, s, e) in enumerate(rows, 1):
+            f.write(f'"KERNEL_DISPATCH",{i},"{name}",{s},{e}\n')
+
+
+def write_counters(d, rows):
+    """rows: (dispatch id, kernel name, start ns, end ns, counter, value); a
+    counter may appear on several rows of one dispatch (its instances)."""
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w") as f:
+        f.write('"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n')
+        for disp, name, s, e, c, v in rows:
+            f.write(f'{disp},"{name}","{c}",{v},{s},{e}\n')
+
+
+def test_kernel_labels():
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.kernel_label(WS_NAME) == "nt_ws_kernel f16 256x256x32 S=4"
+    assert bench.kernel_label(SPLIT_NAME) == "nt_ws_kernel f16 128x128x64 S=3 split"
+    assert bench.kernel_label(RED_NAME) == "reduce_splits f16"
+    assert bench.kernel_label(COPY_NAME) == COPY_NAME
+
+
+def test_summarize_trace_and_counters(tmp_path):
+    d = str(tmp_path / "run")
+    # three dispatches of 800, 820 and 840 us, then a copy kernel
+    write_trace(d, [(WS_NAME, 0, 800_000), (WS_NAME, 1_000_000, 1_820_000), (WS_NAME, 2_000_000, 2_840_000),
+                    (COPY_NAME, 3_000_000, 3_002_000)])
+    # one dispatch of 1000 us: GRBM_GUI_ACTIVE over 8 XCDs = 1.6e6 cycles each
+    # (1.6 GHz), MFMA busy cycles summed over two instances = 0.75 of 1024
+    # SIMDs x 1.6e6
+    busy = 0.75 * 1024 * 1.6e6
+    write_counters(d, [(1, WS_NAME, 0, 1_000_000, "GRBM_GUI_ACTIVE", 8 * 1.6e6),
+                       (1, WS_NAME, 0, 1_000_000, "SQ_VALU_MFMA_BUSY_CYCLES", busy / 2),
+                       (1, WS_NAME, 0, 1_000_000, "SQ_VALU_MFMA_BUSY_CYCLES", busy / 2)])
+    r = run_bench("--summarize", d, "--steps", "2", timeout=60)
+    assert r.returncode == 0, r.stderr
+    rows = {l.split("|")[1].strip(): [c.strip() for c in l.split("|")[2:-1]]
+            for l in r.stdout.splitlines() if l.startswith("| nt_") or l.startswith("| __amd")}
+    trace = [l for l in r.stdout.splitlines() if l.startswith("| nt_ws_kernel")]
+    # trace row: dispatches, mean, min, max, mean of the last two
+    assert trace[0].split("|")[2:7] == [" 3 ", " 820.00 ", " 800.00 ", " 840.00 ", " 830.00 "]
+    # counter row: ..., sclk 1.600, MFMA busy 75.0 %
+    assert trace[1].rstrip(" |").endswith("| 1.600 | 75.0 %")
+    assert rows[COPY_NAME][0] == "1"
+
+
+def test_traffic_reduction(tmp_path):
+    # a 512 MiB device copy reads FETCH_SIZE = 262144 KiB and writes
+    # WRITE_SIZE = 524288 KiB: read scale 2, write scale 1
+    cf, cw = str(tmp_path / "cf"), str(tmp_path / "cw")
+    write_counters(cf, [(1, COPY_NAME, 0, 1, "FETCH_SIZE", 131072), (1, COPY_NAME, 0, 1, "FETCH_SIZE", 131072)])
+    write_counters(cw, [(1, COPY_NAME, 0, 1, "WRITE_SIZE", 524288)])
+    # two timed calls of a K-split product, each a GEMM dispatch and a
+    # reduction, after one warm-up call that must be left out
+    kf, kw = str(tmp_path / "kf"), str(tmp_path / "kw")
+    seq = [(SPLIT_NAME, 999, 999), (RED_NAME, 999, 999), (SPLIT_NAME, 100_000, 8_000), (RED_NAME, 20_000, 2_000),
+           (SPLIT_NAME, 102_000, 8_200), (RED_NAME, 20_000, 1_800)]
+    write_counters(kf, [(i, n, 0, 1, "FETCH_SIZE", f) for i, (n, f, _) in enumerate(seq, 1)])
+    write_counters(kw, [(i, n, 0, 1, "WRITE_SIZE", w) for i, (n, _, w) in enumerate(seq, 1)])
+    r = run_bench("--traffic", kf, kw, cf, cw, "--workload", "f16_nt_skinny", "--variant", "ws", "--stages", "3",
+                  "--steps", "2", timeout=60)
+    assert r.returncode == 0, r.stderr
+    line = [l for l in r.stdout.splitlines() if l.startswith("traffic ")]
+    assert len(line) == 1
+    # per call: fetch (100000 + 20000 + 102000 + 20000) / 2 KiB x 1024 x 2,
+    # write (8000 + 2000 + 8200 + 1800) / 2 KiB x 1024 x 1
+    expect = int(121000 * 1024 * 2 + 10000 * 1024)
+    assert line[0].startswith("traffic nt_ws_kernel f16_nt_skinny S=3 src=")
+    assert line[0].endswith(f"bytes={expect}")
