@@ -13,7 +13,10 @@ for the passages followed and the readings taken):
 * ``gemm_nt(fmt, lhs[M,K], rhs[N,K])`` -> (``ref``, ``mag``) float64 ``[M,N]``:
   ``ref = sum_k a*b`` in k order in binary64, ``mag = sum_k |a*b|``.
 * ``check_nt`` applies the acceptance bound
-  ``|g - ref| <= rel*mag + ulp(RNE(ref))`` in the output format.
+  ``|g - ref| <= rel*mag + ulp(RNE(ref))`` in the output format; a NaN or
+  infinite ``ref`` must come out as NaN or as the same infinity, and an
+  infinite output is accepted for a finite ``ref`` of its sign that lies
+  within the bound of the format's overflow threshold or beyond it.
 """
 from __future__ import annotations
 

@@ -23,6 +23,12 @@
  *   - Output rounding is round-to-nearest-even; the acceptance test for a
  *     GPU element g is |g - ref| <= rel * mag + ulp(RNE(ref)) in the output
  *     type (rel = 1e-3).
+ *   - Special values follow IEEE 754: a NaN or infinite exact sum (a NaN
+ *     operand, an infinity times zero, infinities of both signs, or one
+ *     infinity) must come out as NaN or as that infinity, and a finite sum
+ *     past the output format's overflow threshold as the infinity of its
+ *     sign; subnormal operands count at their value.  pgo_check_nt gives
+ *     the exact rule.
  *
  * Codecs: IEEE-754 binary16 (1 sign, 5 exponent bits with bias 15, 10
  * fraction bits, subnormals) and bfloat16 (the upper half of binary32: 1, 8
@@ -229,24 +235,56 @@ int pgo_gemm_nt_entries(int fmt, const uint16_t *lhs, const uint16_t *rhs,
   return 0;
 }
 
-/* Acceptance test.  Element i passes iff
- *   |decode(got[i]) - ref[i]| <= rel * mag[i] + ulp(RNE(ref[i]))
- * with ulp taken in the output format.  Returns the number of failures
- * (NaN counts as a failure) and the largest |err| / bound in *worst. */
+/* Acceptance test, element by element, in the output format (largest finite
+ * value MAX, spacing of the top binade TOP, overflow threshold
+ * MAX + TOP/2 of round-to-nearest-even).  With r = ref[i] (the exact
+ * products summed in binary64, so NaN or an infinity when IEEE arithmetic
+ * gives one), g = decode(got[i]) and bound = rel * mag[i] + ulp(RNE(r))
+ * (TOP when RNE(r) overflows):
+ *   - r NaN: g must be NaN;
+ *   - r infinite: g must be the same infinity;
+ *   - r finite: g must not be NaN; a finite g must satisfy |g - r| <= bound;
+ *     an infinite g must carry the sign of r, with |r| + bound at or above
+ *     the overflow threshold (the exact sum rounds to it, or is within the
+ *     accumulation error of a sum that does).
+ * Returns the number of failures and, in *worst, the largest |g - r| / bound
+ * over finite pairs (infinity if any element failed otherwise). */
+static double fmt_max(int fmt) { return fmt == PGO_F16 ? 65504.0 : ldexp(255.0, 120); }
+static double fmt_top_ulp(int fmt) { return fmt == PGO_F16 ? 32.0 : ldexp(1.0, 120); }
+
 int64_t pgo_check_nt(int fmt, const uint16_t *got, const double *ref,
                      const double *mag, int64_t count, double rel, double *worst) {
   int64_t bad = 0;
   double w = 0.0;
+  const double top = fmt_top_ulp(fmt), threshold = fmt_max(fmt) + top / 2;
   for (int64_t i = 0; i < count; ++i) {
     double g = fmt == PGO_F16 ? pgo_f16_to_f64(got[i]) : pgo_bf16_to_f64(got[i]);
     double r = ref[i];
-    double yr = fmt == PGO_F16 ? pgo_f16_to_f64(pgo_f64_to_f16(r))
-                               : pgo_bf16_to_f64(pgo_f64_to_bf16(r));
-    double ulp = fmt == PGO_F16 ? pgo_ulp_f16(yr) : pgo_ulp_bf16(yr);
-    double bound = rel * mag[i] + ulp;
-    double err = fabs(g - r);
-    if (!(err <= bound)) ++bad;
-    double ratio = isnan(err) ? INFINITY : err / bound;
+    int ok;
+    double ratio = 0.0;
+    if (isnan(r)) {
+      ok = isnan(g);
+    } else if (isinf(r)) {
+      ok = g == r;
+    } else if (isnan(g)) {
+      ok = 0;
+    } else {
+      double yr = fmt == PGO_F16 ? pgo_f16_to_f64(pgo_f64_to_f16(r))
+                                 : pgo_bf16_to_f64(pgo_f64_to_bf16(r));
+      double ulp = isinf(yr) ? top : fmt == PGO_F16 ? pgo_ulp_f16(yr) : pgo_ulp_bf16(yr);
+      double bound = rel * mag[i] + ulp;
+      if (isinf(g)) {
+        ok = (signbit(g) == signbit(r)) && fabs(r) + bound >= threshold;
+      } else {
+        double err = fabs(g - r);
+        ok = err <= bound;
+        ratio = err / bound;
+      }
+    }
+    if (!ok) {
+      ++bad;
+      ratio = INFINITY;
+    }
     if (ratio > w) w = ratio;
   }
   if (worst) *worst = w;

@@ -145,3 +145,100 @@ def make_operands(kind: str, M: int, N: int, K: int, seed: int):
     if kind == "bf16_nt":
         return bf16_normal((M, K), seed, 0), bf16_normal((N, K), seed, 1)
     raise ValueError(f"unknown operand kind {kind!r}")
+
+
+# Special-value operands (the edge cases of IEEE 754 half-precision input):
+#
+# * "subnormal": rows in three classes by index mod 3, in both operands.
+#   binary16: 0 = every element subnormal (exponent field 0, fraction 1..1023,
+#   random sign), 1 = the uniform recipe, 2 = each element subnormal or
+#   uniform with probability 1/2.  bfloat16: 0 = every element subnormal
+#   (fraction 1..127), 1 = the normal recipe, 2 = the normal recipe times
+#   2**50 (so that subnormal x class 2 products are normal binary32 values,
+#   and no sum leaves binary32's range).
+# * "overflow": binary16: the uniform recipe times 2**7 (sums over a few
+#   hundred k reach past 65504 in both directions); bfloat16: magnitudes of
+#   the normal recipe times 2**(58 + m mod 6) for lhs row m and 2**62 for
+#   every rhs row, lhs rows of odd m negated (every product of an element
+#   has one sign, so sums grow monotonically past the largest finite value).
+# * "nonfinite": the standard recipe with infinities and NaNs planted at
+#   fixed positions (edges of the K range and of the matrices included) and
+#   a zero facing one of the infinities (see ``_plant_nonfinite``).
+# * "zeros": the standard recipe with lhs rows of m mod 4 == 0 set to zeros of
+#   random sign and rhs rows of n mod 5 == 0 set to -0.
+SPECIAL_CASES = ("subnormal", "overflow", "nonfinite", "zeros")
+_SPECIAL = {
+    "f16": {"inf": 0x7C00, "ninf": 0xFC00, "nan": 0x7E00, "frac": 0x3FF, "exp_shift": 10},
+    "bf16": {"inf": 0x7F80, "ninf": 0xFF80, "nan": 0x7FC0, "frac": 0x7F, "exp_shift": 7},
+}
+
+
+def _subnormal_bits(fmt, shape, seed, tensor):
+    n = int(np.prod(shape))
+    x = splitmix64(tensor_key(seed, tensor), 0, n)
+    frac = np.uint64(_SPECIAL[fmt]["frac"])
+    mag = (x % frac + np.uint64(1)).astype(np.uint16)
+    sign = ((x >> np.uint64(63)).astype(np.uint16) << np.uint16(15))
+    return (mag | sign).reshape(shape)
+
+
+def _scale_exponent(fmt, bits, add):
+    """bits times 2**add for normal, nonzero values (exponent field + add)."""
+    bits = np.asarray(bits, np.uint16)
+    shift = _SPECIAL[fmt]["exp_shift"]
+    exp = (bits.astype(np.int64) >> shift) & (0x1F if fmt == "f16" else 0xFF)
+    add = np.broadcast_to(np.asarray(add, np.int64), bits.shape)
+    top = 0x1F if fmt == "f16" else 0xFF
+    if np.any((exp > 0) & (exp + add >= top)):
+        raise ValueError("scaled value leaves the normal range")
+    return np.where(exp > 0, bits.astype(np.int64) + (add << shift), bits).astype(np.uint16)
+
+
+def _plant_nonfinite(fmt, A, B):
+    s = _SPECIAL[fmt]
+    M, K = A.shape
+    N = B.shape[0]
+    A, B = A.copy(), B.copy()
+    k5 = min(5, K - 1)
+    A[1 % M, k5] = s["inf"]
+    A[2 % M, K - 1] = s["ninf"]
+    A[3 % M, 0] = s["nan"]
+    if K >= 2:
+        A[4 % M, K // 2] = s["inf"]
+        A[4 % M, K // 2 - 1] = s["ninf"]
+    A[M - 1, 0] = s["inf"]
+    B[2 % N, k5] = 0            # faces the infinity of lhs row 1
+    B[5 % N, K // 3] = s["inf"]
+    B[6 % N, K - 1] = s["nan"]
+    B[N - 1, K - 1] = s["ninf"]
+    return A, B
+
+
+def special_operands(fmt: str, case: str, M: int, N: int, K: int, seed: int):
+    """(lhs[M,K], rhs[N,K]) half-precision bits for one special-value case."""
+    if fmt not in _SPECIAL or case not in SPECIAL_CASES:
+        raise ValueError(f"unknown special case {fmt!r} {case!r}")
+    A, B = make_operands(f"{fmt}_nt", M, N, K, seed)
+    if case == "subnormal":
+        def classes(X, tensor):
+            sub = _subnormal_bits(fmt, X.shape, seed, 2 + tensor)
+            cls = (np.arange(X.shape[0]) % 3)[:, None]
+            if fmt == "f16":
+                coin = (splitmix64(tensor_key(seed, 4 + tensor), 0, X.size) & np.uint64(1)).reshape(X.shape) == 1
+                return np.where(cls == 0, sub, np.where((cls == 2) & coin, sub, X)).astype(np.uint16)
+            return np.where(cls == 0, sub, np.where(cls == 2, _scale_exponent(fmt, X, 50), X)).astype(np.uint16)
+        return classes(A, 0), classes(B, 1)
+    if case == "overflow":
+        if fmt == "f16":
+            scale = lambda X: (X.view(np.float16).astype(np.float32) * 128.0).astype(np.float16).view(np.uint16)
+            return scale(A), scale(B)
+        m = np.arange(M)[:, None]
+        A = _scale_exponent(fmt, A & np.uint16(0x7FFF), 58 + m % 6) | np.where(m % 2 == 1, 0x8000, 0).astype(np.uint16)
+        B = _scale_exponent(fmt, B & np.uint16(0x7FFF), 62)
+        return A.astype(np.uint16), B.astype(np.uint16)
+    if case == "nonfinite":
+        return _plant_nonfinite(fmt, A, B)
+    zero_sign = ((splitmix64(tensor_key(seed, 6), 0, A.size) & np.uint64(1)).astype(np.uint16) << np.uint16(15))
+    A = np.where((np.arange(M) % 4 == 0)[:, None], zero_sign.reshape(A.shape), A).astype(np.uint16)
+    B = np.where((np.arange(N) % 5 == 0)[:, None], np.uint16(0x8000), B).astype(np.uint16)
+    return A, B

@@ -240,6 +240,49 @@ def _closed_forms(pg, variant, stages):
         assert np.array_equal(run_nt(pg, fmt, variant, u, v, stages), oracle.encode(fmt, ref))
 
 
+# ----------------------------------------------------------- special values
+
+# Several tiles with ragged edges on both tile sizes, and K = 203 (not a
+# multiple of 8: the element-guarded staged loader).
+SPECIAL_SHAPES = [(97, 83, 264), (300, 260, 1000), (65, 70, 203)]
+SPECIAL_RUNS = [("swap", 2), ("swap", 4), ("ws", 3), ("ws", 4)]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("case", inputs.SPECIAL_CASES)
+def test_nt_special_values(pg, fmt, case):
+    # IEEE special values through every loader, schedule, tiling and K split
+    # and the persistent schedule: NaN and infinities where the exact sum has
+    # them, overflow to the infinity of the sum's sign, subnormal operands
+    # (and binary32-subnormal sums for bfloat16) at their value, and sums of
+    # zero products as +0
+    for M, N, K in SPECIAL_SHAPES:
+        A, B = inputs.special_operands(fmt, case, M, N, K, 900 + M + K)
+        ref, mag = oracle.gemm_nt(fmt, A, B)
+        dA, dB = dev_half(A, fmt), dev_half(B, fmt)
+        outs = {}
+        for tile, split in TILINGS + [(0, 0)]:
+            with tiling(pg, tile, split):
+                pieces = pg.pgemm_query("nt_ws", 0, M, N, K)["k_split"]
+                first = None
+                for variant, s in SPECIAL_RUNS:
+                    got = run_nt(pg, fmt, variant, A, B, s, dA, dB)
+                    what = f"{fmt} {case} {variant} S={s} tile {tile} pieces {pieces} {M}x{N}x{K}"
+                    outs[what] = got
+                    if first is None:
+                        first = got
+                    else:
+                        assert np.array_equal(got, first), f"{what} differs in bits from {SPECIAL_RUNS[0]}"
+        with tiling(pg, 128, 1), persistence(pg, 2):
+            outs[f"{fmt} {case} persistent {M}x{N}x{K}"] = run_nt(pg, fmt, "ws", A, B, 4, dA, dB)
+        for what, got in outs.items():
+            assert_within_bound(fmt, got, ref, mag, what)
+            if case == "zeros":
+                assert np.all(got[np.arange(M) % 4 == 0] == 0), f"{what}: a zero lhs row gave a non-+0 bit pattern"
+                assert np.all(got[:, np.arange(N) % 5 == 0] == 0), f"{what}: a -0 rhs row gave a non-+0 bit pattern"
+    assert pg.pgemm_debug_status() == 0
+
+
 # ------------------------------------------------------ full-size workloads
 
 @pytest.fixture(scope="module")

@@ -247,3 +247,77 @@ def test_check_rejects_planted_ring_mistakes():
     got = oracle.encode("f16", ref)
     got[3, 4] = 0x7E00
     assert oracle.check_nt("f16", got, ref, mag)[0] == 1
+
+
+# ------------------------------------------- special values (IEEE 754)
+
+F16_INF, F16_NINF, F16_NAN, F16_MAX = 0x7C00, 0xFC00, 0x7E00, 0x7BFF
+BF16_INF, BF16_NINF, BF16_NAN, BF16_MAX = 0x7F80, 0xFF80, 0x7FC0, 0x7F7F
+NAN, INF = float("nan"), float("inf")
+# (ref, mag, output bits, accepted?) -- overflow threshold 65520 for
+# binary16 (65504 plus half its top-binade spacing of 32), 2**128 - 2**119
+# for bfloat16 (255 * 2**120 plus half of 2**120)
+CHECK_CASES = {
+    "f16": [
+        (NAN, NAN, F16_NAN, True), (NAN, NAN, F16_INF, False), (NAN, NAN, 0x3C00, False),
+        (INF, INF, F16_INF, True), (INF, INF, F16_NINF, False), (INF, INF, F16_MAX, False), (INF, INF, F16_NAN, False),
+        (-INF, INF, F16_NINF, True), (-INF, INF, F16_INF, False),
+        (1e6, 1e6, F16_INF, True), (1e6, 1e6, F16_MAX, False), (1e6, 1e6, F16_NINF, False), (1e6, 1e6, F16_NAN, False),
+        (-1e6, 1e6, F16_NINF, True), (-1e6, 1e6, F16_INF, False),
+        (65520.0, 0.0, F16_INF, True), (65520.0, 0.0, F16_MAX, True),    # the threshold itself rounds up
+        (65519.0, 0.0, F16_INF, True), (65519.0, 0.0, F16_MAX, True),    # one spacing below
+        (65400.0, 0.0, F16_INF, False), (65400.0, 0.0, F16_MAX, False),  # RNE is 65408: three spacings off
+        (60000.0, 60000.0, F16_INF, False), (70000.0, 70000.0, F16_MAX, False),
+        (1.0, 1.0, F16_NAN, False),
+    ],
+    "bf16": [
+        (NAN, NAN, BF16_NAN, True), (NAN, NAN, BF16_INF, False),
+        (INF, INF, BF16_INF, True), (INF, INF, BF16_NINF, False), (INF, INF, BF16_MAX, False),
+        (1e39, 1e39, BF16_INF, True), (1e39, 1e39, BF16_MAX, False), (-1e39, 1e39, BF16_NINF, True),
+        (2.0 ** 128 - 2.0 ** 119, 0.0, BF16_INF, True),
+        (3e38, 3e38, BF16_INF, False), (3.385e38, 0.0, BF16_MAX, True), (3.3e38, 0.0, BF16_MAX, False),
+        (1.0, 1.0, BF16_NAN, False),
+    ],
+}
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_check_special_values(fmt):
+    for r, m, bits, want in CHECK_CASES[fmt]:
+        bad, worst = oracle.check_nt(fmt, np.array([bits], np.uint16), np.array([r]), np.array([m]))
+        assert (bad == 0) == want, (fmt, r, m, hex(bits), want)
+        if not want:
+            assert worst == INF
+    # all at once: the failures are counted, not stopped at
+    rows = CHECK_CASES[fmt]
+    bad, _ = oracle.check_nt(fmt, np.array([b for _, _, b, _ in rows], np.uint16), np.array([r for r, _, _, _ in rows]),
+                             np.array([m for _, m, _, _ in rows]))
+    assert bad == sum(1 for *_, w in rows if not w)
+
+
+def test_oracle_special_products():
+    # IEEE 754 arithmetic fixes these: inf * 0 = NaN, inf - inf = NaN, NaN
+    # propagates, an infinity plus finite terms stays that infinity
+    one, two, five = 0x3C00, 0x4000, 0x4500
+    A = np.array([[F16_INF, one, two], [F16_INF, F16_NINF, 0], [F16_NAN, one, one]], np.uint16)
+    B = np.array([[0, one, one], [one, one, one], [0xBC00, 0, 0], [one, 0xBC00, five]], np.uint16)
+    ref, mag = oracle.gemm_nt("f16", A, B)
+    assert np.isnan(ref[0, 0]) and np.isnan(mag[0, 0])
+    assert ref[0, 1] == INF and mag[0, 1] == INF
+    assert ref[0, 2] == -INF
+    assert ref[0, 3] == INF                      # inf*1 + 1*(-1) + 2*5
+    assert np.isnan(ref[1, 1])                   # inf + (-inf)
+    assert ref[1, 3] == INF                      # inf*1 + (-inf)*(-1)
+    assert np.isnan(ref[1, 2])                   # inf*(-1) + (-inf)*0
+    assert np.all(np.isnan(ref[2]))
+    assert oracle.encode("f16", ref[0:2, 0:4]).tolist() == [[F16_NAN, F16_INF, F16_NINF, F16_INF],
+                                                             [F16_NAN, F16_NAN, F16_NAN, F16_INF]]
+    # subnormal operands count at their value; their products are exact in binary64
+    ref, _ = oracle.gemm_nt("f16", np.array([[0x0001, 0x03FF]], np.uint16), np.array([[0x0001, 0x3C00]], np.uint16))
+    assert ref[0, 0] == 2.0 ** -48 + 1023 * 2.0 ** -24
+    ref, _ = oracle.gemm_nt("bf16", np.array([[0x0001, 0x007F]], np.uint16), np.array([[0x0001, 0x4F80]], np.uint16))
+    assert ref[0, 0] == 2.0 ** -266 + 127 * 2.0 ** -133 * 2.0 ** 32
+    # zero products: the sum starts at +0, so only +0 comes out
+    ref, mag = oracle.gemm_nt("f16", np.full((1, 4), 0x8000, np.uint16), np.full((1, 4), one, np.uint16))
+    assert ref[0, 0] == 0 and not np.signbit(ref[0, 0]) and mag[0, 0] == 0
+    assert oracle.encode("f16", ref).tolist() == [[0]]
