@@ -226,6 +226,18 @@ pgemm_status pgemm_set_persistent(int mode);
  * needs: without the seeds the first producer wait can never succeed). */
 void pgemm_set_ws_debug(int64_t max_polls, int skip_seed);
 
+/* Test hook for the credit protocol (Croqtile ch.6, "credit flow of a single
+ * stage": a consumer may only read a slot its producer has filled, and a
+ * producer may only refill a slot its consumers have released, whatever
+ * the timing).  A non-zero seed (its low 31 bits) makes every wave of later
+ * *_ws launches in this process sleep a pseudo-random 0 to 1792 clocks
+ * before each of its credit waits and triggers.  The count depends on the
+ * seed, the workgroup, the wave, the K tile and the site, so producers and
+ * consumers meet in orders their natural timing does not give.  The
+ * results must not change.  0 turns it off (the default), leaving one
+ * scalar compare per credit operation. */
+void pgemm_set_ws_jitter(uint32_t seed);
+
 /*
  * Pipeline planner (host only, no HIP call), the rules the library applies
  * to size each kernel's LDS ring (TileLang ch.22, "pipeline-sync-

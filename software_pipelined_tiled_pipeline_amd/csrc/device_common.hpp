@@ -155,6 +155,28 @@ __device__ __forceinline__ void credit_trigger(uint32_t *ctr) {
     asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(ctr)), "v"(1u) : "memory");
 }
 
+// Timing jitter for testing the credit protocol.  A producer/consumer
+// launch takes a debug word: bit 0 skips the seeding of `empty` (the
+// protocol then cannot start, and the bounded waits give up), and bits 1-31
+// hold a jitter seed.  With a non-zero seed, each wave sleeps 0 to 7 times
+// 256 clocks before each credit operation.  The count is a hash of the seed,
+// the workgroup, the wave, the position in the K sequence and the call site,
+// so producers and consumers meet in orders their natural timing does not
+// give, while the results must stay the same.  The hash is lowbias32
+// (C. Wellons, "Hash function prospector", 2018).  With seed 0 the cost is
+// one scalar compare per site.
+__device__ __forceinline__ void jitter_sleep(uint32_t seed, int wave, uint32_t pos, uint32_t site) {
+  if (seed) {
+    uint32_t h = seed ^ (blockIdx.x * 0x9E3779B9u) ^ ((uint32_t)wave << 24) ^ (pos * 4u + site);
+    h ^= h >> 16;
+    h *= 0x7FEB352Du;
+    h ^= h >> 15;
+    h *= 0x846CA68Bu;
+    h ^= h >> 16;
+    for (uint32_t i = 0, n = h & 7u; i < n; ++i) __builtin_amdgcn_s_sleep(4);
+  }
+}
+
 __device__ __forceinline__ void credit_wait(const uint32_t *ctr, uint32_t target, uint32_t max_polls,
                                             uint32_t *err) {
   uint32_t polls = 0;

@@ -547,7 +547,7 @@ template <typename T, class G, bool SPLIT, bool STAGED>
 __global__ void __launch_bounds__(G::THREADS)
     nt_ws_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
                  uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m,
-                 int k_chunk, float *__restrict__ partial, int ldp, uint32_t max_polls, int skip_seed,
+                 int k_chunk, float *__restrict__ partial, int ldp, uint32_t max_polls, uint32_t debug,
                  uint32_t *err) {
   static_assert(G::P > 0, "producer/consumer kernel needs producer waves");
   // Arguments used only inside or after the K loop are read into SGPRs up
@@ -555,6 +555,8 @@ __global__ void __launch_bounds__(G::THREADS)
   // return out of order) turns the first fragment wait of every tile into a
   // wait for all outstanding LDS reads.
   __asm__ volatile("" ::"s"(out), "s"(partial), "s"(ldp), "s"(err), "s"(max_polls));
+  const bool skip_seed = debug & 1u;  // test hooks (see jitter_sleep)
+  const uint32_t jit = debug >> 1;
   using Loader = std::conditional_t<STAGED, StagedLoader<G::BM, G::BN, G::BK>, typename G::Loader>;
   using Row = RingRow<G::BK>;
   constexpr int S = G::S, C = G::CW, P = G::P;
@@ -614,6 +616,7 @@ __global__ void __launch_bounds__(G::THREADS)
       typename W::Frags f[2];
       NoLoads no_load;
       if (n_k > 0) {
+        jitter_sleep(jit, wave, 0, 1);
         credit_wait(&full[0], (uint32_t)FP, max_polls, err);
         W::read_frags(f[0], lane_a(0), lane_b(0), 0, chunk, sw);
       }
@@ -627,8 +630,10 @@ __global__ void __launch_bounds__(G::THREADS)
           w.template mixed_step<true, 0>(f[(F0 + kk) & 1], f[(F0 + kk + 1) & 1], lane_a(s), lane_b(s), kk + 1,
                                          chunk, sw, no_load);
         wait_lgkmcnt0();  // the last fragment reads of slot s are done
+        jitter_sleep(jit, wave, t, 0);
         credit_trigger(&empty[s]);
         const uint32_t target = (uint32_t)FP * ((uint32_t)((t + 1) / S) + 1u);
+        jitter_sleep(jit, wave, t + 1, 1);
         if (t + 1 < n_k && __builtin_amdgcn_readfirstlane(next) < target)
           credit_wait(&full[s1], target, max_polls, err);
         w.template mixed_step<true, 0>(f[(F0 + NK - 1) & 1], f[(F0 + NK) & 1], lane_a(s1), lane_b(s1), 0, chunk,
@@ -653,6 +658,7 @@ __global__ void __launch_bounds__(G::THREADS)
       for (int t = 0; t < n_k; ++t) {
         const int s = t % S;
         const uint32_t target = (uint32_t)FP * ((uint32_t)(t / S) + 1u);
+        jitter_sleep(jit, wave, t, 1);
         if (seen < target) credit_wait(&full[s], target, max_polls, err);
         compiler_fence();
         const uint32_t next = t + 1 < n_k ? credit_load(&full[(t + 1) % S]) : 0u;
@@ -660,6 +666,7 @@ __global__ void __launch_bounds__(G::THREADS)
         w.template mma_ktile<2>(base + wm * G::WM * Row::ROW_BYTES, base + (G::BM + wn * G::WN) * Row::ROW_BYTES,
                                 lane);
         wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
+        jitter_sleep(jit, wave, t, 0);
         credit_trigger(&empty[s]);
         seen = __builtin_amdgcn_readfirstlane(next);
       }
@@ -677,12 +684,14 @@ __global__ void __launch_bounds__(G::THREADS)
       // at once, and no `full` waits for a later tile's slot to come free.
       for (int t = wave - C; t < n_k; t += P) {
         const int s = t % S;
+        jitter_sleep(jit, wave, t, 2);
         credit_wait(&empty[s], (uint32_t)C * ((uint32_t)(t / S) + 1u), max_polls, err);
         ld.template load<Loader::INSTR>(slot_ptr(s), t, 0, lane);
         if constexpr (Loader::DIRECT)
           wait_vmcnt<0>();  // tile t landed
         else
           wait_lgkmcnt0();  // this wave's writes of tile t are done
+        jitter_sleep(jit, wave, t, 3);
         credit_trigger(&full[s]);
       }
     } else {
@@ -700,6 +709,7 @@ __global__ void __launch_bounds__(G::THREADS)
       static_assert((LAG + 1) * PER < 64, "loads in flight fit the 6-bit vmcnt");
       for (int t = 0; t < n_k; ++t) {
         const int s = t % S;
+        jitter_sleep(jit, wave, t, 2);
         credit_wait(&empty[s], (uint32_t)C * ((uint32_t)(t / S) + 1u), max_polls, err);
         ld.template load<PER>(slot_ptr(s), t, first, lane);
         if (t >= LAG) {
@@ -707,18 +717,21 @@ __global__ void __launch_bounds__(G::THREADS)
             wait_vmcnt<LAG * PER>();  // tile t - LAG landed
           else
             wait_lgkmcnt0();  // this wave's writes of tile t are done
+          jitter_sleep(jit, wave, t, 3);
           credit_trigger(&full[(t - LAG) % S]);
         }
       }
       if constexpr (LAG >= 2) {
         if (n_k >= 2) {
           wait_vmcnt<PER>();
+          jitter_sleep(jit, wave, n_k, 3);
           credit_trigger(&full[(n_k - 2) % S]);
         }
       }
       if constexpr (LAG >= 1) {
         if (n_k >= 1) {
           wait_vmcnt<0>();
+          jitter_sleep(jit, wave, n_k + 1, 3);
           credit_trigger(&full[(n_k - 1) % S]);
         }
       }
@@ -751,9 +764,11 @@ template <typename T, class G>
 __global__ void __launch_bounds__(G::THREADS)
     nt_ws_persistent_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
                             uint16_t *__restrict__ out, int M, int N, int K, int tiles_m, int tiles_n, int group_m,
-                            uint32_t max_polls, int skip_seed, uint32_t *err) {
+                            uint32_t max_polls, uint32_t debug, uint32_t *err) {
   static_assert(G::P > 0, "producer/consumer kernel needs producer waves");
   __asm__ volatile("" ::"s"(out), "s"(err), "s"(max_polls));  // see nt_ws_kernel
+  const bool skip_seed = debug & 1u;
+  const uint32_t jit = debug >> 1;
   using Loader = typename G::Loader;
   using Row = RingRow<G::BK>;
   constexpr int S = G::S, C = G::CW, P = G::P;
@@ -797,6 +812,7 @@ __global__ void __launch_bounds__(G::THREADS)
       for (int t = 0; t < n_k; ++t, ++g) {
         const int s = (int)(g % S);
         const uint32_t target = (uint32_t)FP * (g / S + 1u);
+        jitter_sleep(jit, wave, g, 1);
         if (seen < target) credit_wait(&full[s], target, max_polls, err);
         compiler_fence();
         const uint32_t next = g + 1 < total ? credit_load(&full[(g + 1) % S]) : 0u;
@@ -804,6 +820,7 @@ __global__ void __launch_bounds__(G::THREADS)
         w.template mma_ktile<(G::WM > 64 ? 2 : 1)>(base + wm * G::WM * Row::ROW_BYTES,
                                                     base + (G::BM + wn * G::WN) * Row::ROW_BYTES, lane);
         wait_lgkmcnt0();  // this slot's fragment reads are done (MFMAs read registers)
+        jitter_sleep(jit, wave, g, 0);
         credit_trigger(&empty[s]);
         seen = __builtin_amdgcn_readfirstlane(next);
       }
@@ -829,9 +846,11 @@ __global__ void __launch_bounds__(G::THREADS)
           cur = it;
         }
         const int s = (int)(g % S);
+        jitter_sleep(jit, wave, g, 2);
         credit_wait(&empty[s], (uint32_t)C * (g / S + 1u), max_polls, err);
         ld.template load<Loader::INSTR>(slot_ptr(s), t, 0, lane);
         wait_vmcnt<0>();  // entry g landed
+        jitter_sleep(jit, wave, g, 3);
         credit_trigger(&full[s]);
       }
     } else {
@@ -850,10 +869,12 @@ __global__ void __launch_bounds__(G::THREADS)
         ld.init(lhs, rhs, M, N, K, 0, K, bm * G::BM, bn * G::BN);
         for (int t = 0; t < n_k; ++t, ++g) {
           const int s = (int)(g % S);
+          jitter_sleep(jit, wave, g, 2);
           credit_wait(&empty[s], (uint32_t)C * (g / S + 1u), max_polls, err);
           ld.template load<PER>(slot_ptr(s), t, first, lane);
           if (g >= (uint32_t)LAG) {
             wait_vmcnt<LAG * PER>();  // entry g - LAG landed
+            jitter_sleep(jit, wave, g, 3);
             credit_trigger(&full[(g - LAG) % S]);
           }
         }
@@ -861,12 +882,14 @@ __global__ void __launch_bounds__(G::THREADS)
       if constexpr (LAG >= 2) {
         if (g >= 2) {
           wait_vmcnt<PER>();
+          jitter_sleep(jit, wave, g, 3);
           credit_trigger(&full[(g - 2) % S]);
         }
       }
       if constexpr (LAG >= 1) {
         if (g >= 1) {
           wait_vmcnt<0>();
+          jitter_sleep(jit, wave, g + 1, 3);
           credit_trigger(&full[(g - 1) % S]);
         }
       }

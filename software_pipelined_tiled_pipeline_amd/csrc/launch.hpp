@@ -29,7 +29,8 @@ struct NtLaunch {
   hipStream_t stream;
   int dev;           // current device (below 64)
   uint32_t polls;    // poll limit of a credit wait
-  int skip_seed;     // test hook: consumers do not seed `empty`
+  uint32_t debug;    // test hooks: bit 0, consumers do not seed `empty`;
+                     // bits 1-31, a credit-timing jitter seed (0: none)
   uint32_t *err;     // device error word
 };
 

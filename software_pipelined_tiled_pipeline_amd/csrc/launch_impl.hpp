@@ -36,7 +36,7 @@ pgemm_status launch_nt(const NtLaunch &a) {
     pgemm_status st = allow_lds(kern, G::LDS_BYTES, a.dev, lds_set);
     if (st != PGEMM_OK) return st;
     hipLaunchKernelGGL(kern, grid, dim3(G::THREADS), G::LDS_BYTES, a.stream, a.lhs, a.rhs, a.out, a.M, a.N, a.K, tm,
-                       tn, kGroupM, a.k_chunk, a.part, a.ldp, a.polls, a.skip_seed, a.err);
+                       tn, kGroupM, a.k_chunk, a.part, a.ldp, a.polls, a.debug, a.err);
   } else {
     auto kern = nt_swap_kernel<T, G, SPLIT, STAGED>;
     pgemm_status st = allow_lds(kern, G::LDS_BYTES, a.dev, lds_set);
@@ -61,7 +61,7 @@ pgemm_status launch_ws_persistent(const NtLaunch &a) {
   if (st != PGEMM_OK) return st;
   const int tm = cdiv_i(a.M, G::BM), tn = cdiv_i(a.N, G::BN);
   hipLaunchKernelGGL(kern, dim3((unsigned)a.grid), dim3(G::THREADS), G::LDS_BYTES, a.stream, a.lhs, a.rhs, a.out, a.M,
-                     a.N, a.K, tm, tn, kGroupM, a.polls, a.skip_seed, a.err);
+                     a.N, a.K, tm, tn, kGroupM, a.polls, a.debug, a.err);
   return launched();
 }
 

@@ -44,6 +44,7 @@ constexpr uint32_t kDefaultPolls = 1u << 24;
 
 std::atomic<uint32_t> g_max_polls{kDefaultPolls};
 std::atomic<int> g_skip_seed{0};
+std::atomic<uint32_t> g_jitter{0};
 
 // ------------------------------------------------------------- planning
 //
@@ -363,7 +364,8 @@ pgemm_status nt_entry(Elem e, pgemm_op op, const uint16_t *lhs, const uint16_t *
   a.stream = static_cast<hipStream_t>(stream);
   a.dev = dev;
   a.polls = g_max_polls.load(std::memory_order_relaxed);
-  a.skip_seed = g_skip_seed.load(std::memory_order_relaxed);
+  a.debug = (g_skip_seed.load(std::memory_order_relaxed) ? 1u : 0u) |
+            (g_jitter.load(std::memory_order_relaxed) << 1);
   a.err = g_err_ptr[dev];
   return launch(e, a, p.staged);
 }
@@ -520,6 +522,8 @@ void pgemm_set_ws_debug(int64_t max_polls, int skip_seed) {
   g_max_polls.store(p, std::memory_order_relaxed);
   g_skip_seed.store(skip_seed ? 1 : 0, std::memory_order_relaxed);
 }
+
+void pgemm_set_ws_jitter(uint32_t seed) { g_jitter.store(seed & 0x7FFFFFFFu, std::memory_order_relaxed); }
 
 const char *pgemm_strerror(pgemm_status status) {
   switch (status) {

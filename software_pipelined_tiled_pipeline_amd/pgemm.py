@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.pgemm_set_persistent.restype = I
         L.pgemm_set_ws_debug.argtypes = [I64, I]
         L.pgemm_set_ws_debug.restype = None
+        L.pgemm_set_ws_jitter.argtypes = [ctypes.c_uint32]
+        L.pgemm_set_ws_jitter.restype = None
         L.pgemm_strerror.argtypes = [I]
         L.pgemm_strerror.restype = ctypes.c_char_p
         L.pgemm_abi_version.argtypes = []
@@ -224,3 +226,8 @@ def pgemm_set_persistent(mode: int = 0) -> None:
 
 def pgemm_set_ws_debug(max_polls: int = 0, skip_seed: bool = False) -> None:
     lib().pgemm_set_ws_debug(int(max_polls), 1 if skip_seed else 0)
+
+
+def pgemm_set_ws_jitter(seed: int = 0) -> None:
+    """Credit-timing jitter of later producer/consumer calls (0: off)."""
+    lib().pgemm_set_ws_jitter(int(seed) & 0x7FFFFFFF)

@@ -240,6 +240,36 @@ def _closed_forms(pg, variant, stages):
         assert np.array_equal(run_nt(pg, fmt, variant, u, v, stages), oracle.encode(fmt, ref))
 
 
+# ------------------------------------------------------ tile boundaries
+
+# Every K tail of both K tile depths (32 and 64) and of the element-guarded
+# loader (K not a multiple of 8), n_k from 1 to 4 (fewer K tiles than the
+# ring has slots at S = 3, 4), on output tiles cut one row or column short,
+# exact, or one over.
+BOUNDARY_K = [1, 7, 8, 24, 32, 33, 40, 56, 64, 65, 72, 96, 136, 200]
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("dm,dn", [(-1, -1), (-1, 0), (-1, 1), (0, -1), (0, 0), (0, 1), (1, -1), (1, 0), (1, 1)])
+def test_nt_tile_boundaries(pg, tile, dm, dn):
+    M, N = tile + dm, tile + dn
+    for K in BOUNDARY_K:
+        fmt = "f16" if K % 2 else "bf16"
+        A, B = inputs.make_operands(f"{fmt}_nt", M, N, K, 4000 + 7 * K + dm + 3 * dn)
+        ref, mag = oracle.gemm_nt(fmt, A, B)
+        dA, dB = dev_half(A, fmt), dev_half(B, fmt)
+        first = None
+        with tiling(pg, tile, 1):
+            for variant, s in VARIANTS:
+                got = run_nt(pg, fmt, variant, A, B, s, dA, dB)
+                what = f"{fmt} {variant} S={s} tile {tile} {M}x{N}x{K}"
+                assert_within_bound(fmt, got, ref, mag, what)
+                if first is None:
+                    first = got
+                else:
+                    assert np.array_equal(got, first), f"{what} differs in bits from swap S=1"
+
+
 # ----------------------------------------------------------- special values
 
 # Several tiles with ragged edges on both tile sizes, and K = 203 (not a
@@ -533,3 +563,41 @@ def test_missing_seed_times_out_instead_of_hanging(pg):
         assert pg.pgemm_debug_status() == 0
         got = run_nt(pg, "f16", "ws", A, B, 2, dA, dB)
     assert_within_bound("f16", got, ref, mag, "persistent, after reset")
+
+
+@contextlib.contextmanager
+def credit_jitter(pg, seed):
+    pg.pgemm_set_ws_jitter(seed)
+    try:
+        yield
+    finally:
+        pg.pgemm_set_ws_jitter(0)
+
+
+# (tile, k_split, persistent mode, M, N, K): every producer/consumer code
+# path -- whole tiles per producer (32-deep slots) and tiles shared by all
+# producers (64-deep), consumers with one and with two fragment sets, a K
+# split, and the persistent schedule on both tile sizes
+JITTER_CASES = [(256, 1, 0, 700, 600, 520), (128, 1, 0, 700, 650, 1000), (128, 3, 0, 300, 260, 1000),
+                (256, 1, 2, 1100, 1030, 264), (128, 1, 2, 700, 650, 200)]
+
+
+@pytest.mark.parametrize("case", JITTER_CASES, ids=lambda c: "t{}s{}p{}-{}x{}x{}".format(*c))
+def test_ws_credit_jitter_keeps_bits(pg, case):
+    # Random sleeps before every credit wait and trigger make producers and
+    # consumers meet in other orders than their natural timing gives; every
+    # stage count must still give the same bits, and no wait may give up.
+    tile, split, persist, M, N, K = case
+    fmt = "bf16" if tile == 128 else "f16"
+    A, B = inputs.make_operands(f"{fmt}_nt", M, N, K, 600 + M + K)
+    dA, dB = dev_half(A, fmt), dev_half(B, fmt)
+    assert pg.pgemm_debug_status() == 0
+    with tiling(pg, tile, split), persistence(pg, persist):
+        for S in (1, 2, 3, 4):
+            want = run_nt(pg, fmt, "ws", A, B, S, dA, dB)
+            for seed in (1, 0x5A5A5, 0x7FFFFFFF):
+                with credit_jitter(pg, seed):
+                    got = run_nt(pg, fmt, "ws", A, B, S, dA, dB)
+                assert np.array_equal(got, want), f"S={S} jitter seed {seed:#x} changed the bits"
+            assert pg.pgemm_debug_status() == 0
+    check_whole(fmt, A, B, {"jittered": got})
