@@ -416,6 +416,20 @@ struct NtGeom {
 // only step; the fragment sets then alternate per tile, so the loop body
 // covers two tiles.  S = 1 has a single slot and runs fill -> barrier ->
 // compute -> barrier.
+// Two barriers per tile for the two-slot ring of 64-deep tiles on the large
+// tile (64 MFMAs per wave and k32 step).  With one barrier, the refill of
+// tile t's slot can start only at that barrier (the start of tile t's last
+// step) and must land by the next one, one tile later; the loads, issued
+// over the first of those two steps, then have about one step to land, and
+// waves waited for them on most tiles.  Yet the slot is free as soon as
+// tile t's last fragments have been read (halfway through its first step),
+// and tile t+2 is first read only in the second half of tile t+1's last
+// step.  A WAR barrier at the first point and a RAW barrier at the second
+// give the refill about three steps, from half a step after its first load
+// to one and a half after its last.
+template <class G, class Loader, class W>
+constexpr bool kSplitSync = G::P == 0 && G::S == 2 && Loader::DIRECT && W::NK == 2 && W::TM * W::TN == 64;
+
 template <typename T, class G, bool SPLIT, bool STAGED>
 __global__ void __launch_bounds__(G::THREADS, G::OCC)
     nt_swap_kernel(const uint16_t *__restrict__ lhs, const uint16_t *__restrict__ rhs,
@@ -466,6 +480,39 @@ __global__ void __launch_bounds__(G::THREADS, G::OCC)
         w.mma_step(f);
       }
       lds_barrier();
+    }
+  } else if constexpr (kSplitSync<G, Loader, W>) {
+    // Two slots of 64-deep tiles, two barriers per tile (see kSplitSync):
+    //   step 0 of tile t (f[0]): reads of tile t's step 1 into f[1] over the
+    //     first half; WAR barrier once they have landed (slot t is free
+    //     everywhere); then the first loads of tile t+2 into slot t;
+    //   step 1 of tile t (f[1]): the rest of those loads; RAW barrier once
+    //     this wave's loads of tile t+1 have landed (tile t+1 is complete);
+    //     then the reads of tile t+1's step 0 into f[0].
+    // Every tile runs the same two steps, the last ones included (their
+    // loads read zeros into slots that are not read again, and the last
+    // reads are never used): one code path keeps the accumulators in place.
+    constexpr int PER = G::PER_LOADER;
+    static_assert(PER == 16, "the load placement below assumes 16 loads per wave and tile");
+    typename W::Frags f[2];
+    for (int j = 0; j < 2; ++j) ld.template load<PER>(slot_ptr(j), j, first, lane);
+    wait_vmcnt<PER>();  // tile 0 landed
+    lds_barrier();
+    if (n_k > 0) W::read_frags(f[0], lane_a(0), lane_b(0), 0, chunk, sw);
+    auto war = []() __attribute__((always_inline)) { lds_barrier(); };
+    auto raw = []() __attribute__((always_inline)) {
+      wait_vmcnt<PER>();  // still in flight: the 16 loads of tile t+2
+      __builtin_amdgcn_s_barrier();
+    };
+    const int p1 = ((4 + chunk) ^ sw) * 16, p0 = (chunk ^ sw) * 16;
+    for (int t = 0; t < n_k; ++t) {
+      const int s = t & 1, s1 = s ^ 1;
+      RefillLoads<Loader> refill{ld, slot_ptr(s), t + 2, first};
+      auto refill_rest = [&](int i) __attribute__((always_inline)) { refill(i + 6); };
+      w.template sched_step<1, 2, 16, 42, 4, 6, 40>(
+          f[0], typename W::FragReads{f[1], lane_a(s), lane_b(s), p1}, refill, war);
+      w.template sched_step<45, 1, 16, 2, 4, 10, 44>(
+          f[1], typename W::FragReads{f[0], lane_a(s1), lane_b(s1), p0}, refill_rest, raw);
     }
   } else {
     // The prologue issues tiles 0 .. S-1.  Loads of tiles at or past the

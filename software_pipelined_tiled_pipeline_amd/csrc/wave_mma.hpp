@@ -214,6 +214,48 @@ struct WaveTile {
       }
   }
 
+  // Fragment reads for sched_step: call r reads piece r of the next step
+  // (the TN rhs pieces, then the TM lhs pieces) into `nf`.
+  struct FragReads {
+    Frags &nf;
+    const char *lane_a, *lane_b;
+    int p;  // byte offset of the lane's chunk: ((4 kk + chunk) ^ swz) * 16
+    __device__ __forceinline__ void operator()(int r) const {
+      if (r < TN)
+        nf.b[r] = *reinterpret_cast<const u32x4 *>(lane_b + 16 * r * Row::ROW_BYTES + p);
+      else
+        nf.a[r - TN] = *reinterpret_cast<const u32x4 *>(lane_a + 16 * (r - TN) * Row::ROW_BYTES + p);
+    }
+  };
+
+  // One k32 step: the TM*TN MFMAs on `cf` in the fixed order, with other
+  // work at fixed MFMA indices: NRD calls rd(0 .. NRD-1), one every RE
+  // MFMAs from MFMA R0 on; NLD calls ld(0 .. NLD-1), one every LE MFMAs
+  // from L0 on; and sync() right before MFMA SYNC (never when SYNC < 0).
+  // sched_barrier(0) after every MFMA pins the order.
+  template <int R0, int RE, int NRD, int L0, int LE, int NLD, int SYNC, class RdFn, class LdFn, class SyncFn>
+  __device__ __forceinline__ void sched_step(const Frags &cf, RdFn &&rd, LdFn &&ld, SyncFn &&sync) {
+    constexpr int NM = TM * TN;
+    static_assert(NRD == 0 || R0 + (NRD - 1) * RE < NM, "reads fit in the step");
+    static_assert(NLD == 0 || L0 + (NLD - 1) * LE < NM, "loads fit in the step");
+    static_assert(SYNC < NM, "sync point inside the step");
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int m = i * TN + j;
+        if (m == SYNC) sync();
+        Mfma<T>::template run<ACC_AGPR>(cf.b[j], cf.a[i], acc[i][j]);
+        if constexpr (NRD > 0) {
+          if (m >= R0 && (m - R0) % RE == 0 && (m - R0) / RE < NRD) rd((m - R0) / RE);
+        }
+        if constexpr (NLD > 0) {
+          if (m >= L0 && (m - L0) % LE == 0 && (m - L0) / LE < NLD) ld((m - L0) / LE);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+
   // Writes the fp32 accumulators, unrounded, to a row-major partial-sum
   // matrix (row pitch ldp floats, a multiple of 4) at (row0, col0); rows
   // past M and column groups past N are skipped.  Each lane stores its four
