@@ -6,7 +6,8 @@
 //  nt_swap_kernel f16/bf16 NT, one schedule for all waves: every wave runs
 //                 MFMA on tile t and, in tile t's last k32 step, refills
 //                 tile t's slot with its share of tile t+S (direct-to-LDS
-//                 loads); one workgroup barrier per tile.
+//                 loads); one workgroup barrier per tile (two on the
+//                 large tile's two-slot ring, see kSplitSync).
 //  nt_ws_kernel   f16/bf16 NT, producer waves and consumer waves coordinated
 //                 by per-slot full/empty credit counters in LDS.
 //  nt_ws_persistent_kernel
@@ -415,7 +416,8 @@ struct NtGeom {
 // A tile of a single k32 step (BK = 32) has its barrier at the start of its
 // only step; the fragment sets then alternate per tile, so the loop body
 // covers two tiles.  S = 1 has a single slot and runs fill -> barrier ->
-// compute -> barrier.
+// compute -> barrier.  The 256 x 256 tile with two 64-deep slots splits the
+// barrier in two (kSplitSync).
 // Two barriers per tile for the two-slot ring of 64-deep tiles on the large
 // tile (64 MFMAs per wave and k32 step).  With one barrier, the refill of
 // tile t's slot can start only at that barrier (the start of tile t's last
