@@ -308,7 +308,7 @@ struct WaveTile {
         uint16_t *rp = out + (int64_t)row * N;
         const int col = col0 + 16 * (j + odd) + 8 * (g >> 1);
         if (vec_ok && col + 8 <= N) {
-          *reinterpret_cast<u32x4 *>(rp + col) = v;
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(rp + col));
         } else {
 #pragma unroll
           for (int x = 0; x < 8; ++x)
@@ -339,6 +339,15 @@ struct WaveTile {
 // Copies a staged BM x BN tile (2-byte elements, row pitch `pitch` bytes) to
 // out[m0.., n0..] with 16-byte stores where the row piece is in range and
 // aligned, element stores at a ragged right edge, nothing past M.
+//
+// The 16-byte output stores (here and in WaveTile::store_direct) are
+// non-temporal: the output is not read again by the kernel, and the tiles
+// resident on one XCD at a time write as much output as its L2 holds (32
+// tiles of 256 x 256 f16 = 4 MiB), which with ordinary stores pushes the
+// lhs and rhs panels of the next tiles out of L2.  Measured: f16 8192^3
+// single schedule S = 2 +3-6 %, producer/consumer unchanged, 4096^3 up to
+// +1 %.  K-split partial sums keep ordinary stores (reduce_splits reads them
+// right after).
 template <int BM, int BN, int THREADS>
 __device__ __forceinline__ void store_staged(const char *st, int pitch, uint16_t *out, int M, int N,
                                              int m0, int n0, int tid) {
@@ -353,7 +362,7 @@ __device__ __forceinline__ void store_staged(const char *st, int pitch, uint16_t
     const u32x4 v = *reinterpret_cast<const u32x4 *>(st + row * pitch + c * 16);
     uint16_t *dst = out + (int64_t)gm * N + gn;
     if (vec_ok && gn + 8 <= N) {
-      *reinterpret_cast<u32x4 *>(dst) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
     } else {
 #pragma unroll
       for (int x = 0; x < 8; ++x)
