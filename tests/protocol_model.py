@@ -6,7 +6,9 @@ per-wave instruction lists, the schedules that the kernels run:
 * single schedule (Croqtile ch.6, "double buffering with swap", with the
   handles rotated over S slots): every wave issues asynchronous loads of its
   share of a tile into ring slot t mod S, waits for its own loads, meets the
-  other waves at a workgroup barrier, and reads the slot;
+  other waves at a workgroup barrier, and reads the slot; on the large
+  tile's two-slot ring the barrier is split into a WAR barrier (the slot
+  just read is free) and a RAW barrier (the next tile has landed);
 * producer/consumer (Croqtile ch.6, "1P1C kernel with events" and the credit
   flow of one stage; Croqtile ch.5, the bootstrap protocol): producers wait
   for the slot's `empty` credit, load their share asynchronously, and add
@@ -162,7 +164,7 @@ def _consumers(S, ct, C, fp, bootstrap, no_sync, early_release, read_after_last)
 
 
 def swap_programs(S: int, n_k: int, W: int, *, skip_barrier: bool = False, skip_wait: bool = False,
-                  refill_before_barrier: bool = False):
+                  refill_before_barrier: bool = False, split_sync: bool = False, skip_raw_barrier: bool = False):
     """Single schedule with W waves, as the kernels run it.
 
     Each wave's share of a tile is two halves (shares 2w and 2w + 1), issued
@@ -175,7 +177,21 @@ def swap_programs(S: int, n_k: int, W: int, *, skip_barrier: bool = False, skip_
 
     Faults: skip_barrier drops the per-tile barrier; skip_wait drops the
     wait for the wave's own loads; refill_before_barrier issues the refill
-    of tile t's slot before the barrier instead of after it."""
+    of tile t's slot before the barrier instead of after it.
+
+    split_sync (S = 2, the large tile's two-slot ring): a tile's reads are
+    two parts, its first k32 step (read at the end of the previous tile)
+    and its second (read at the start of its own).  After the second part
+    a WAR barrier frees the tile's slot and the wave issues both halves of
+    tile t+2 into it; then it waits for its own loads of tile t+1, meets
+    the others at a RAW barrier and reads tile t+1's first part.  The last
+    tile also reads the first part of tile n_k (loads of tiles past the end
+    are issued too; the data is never used).  Only the second part of a
+    read counts as reading the tile.  Faults: skip_barrier drops the WAR
+    barrier, skip_raw_barrier the RAW barrier, skip_wait the wait before
+    it, refill_before_barrier issues the refill before the WAR barrier."""
+    if split_sync:
+        return _split_sync_programs(n_k, W, skip_barrier, skip_wait, refill_before_barrier, skip_raw_barrier)
     progs = []
     for w in range(W):
         a, b = 2 * w, 2 * w + 1
@@ -213,6 +229,36 @@ def swap_programs(S: int, n_k: int, W: int, *, skip_barrier: bool = False, skip_
                 if not refill_before_barrier:
                     prog += refill
         prog.append((WAITLOADS, 10 ** 9))  # the epilogue waits for every load
+        progs.append(prog)
+    return progs, 2 * W
+
+
+def _split_sync_programs(n_k, W, skip_war, skip_wait, refill_before_war, skip_raw):
+    progs = []
+    for w in range(W):
+        a, b = 2 * w, 2 * w + 1
+        nb = 0
+        prog = [(ISSUE, 0, 0, a), (ISSUE, 0, 0, b), (ISSUE, 1, 1, a), (ISSUE, 1, 1, b)]
+        if not skip_wait:
+            prog.append((WAITLOADS, 0))
+        prog.append((BARRIER, nb)); nb += 1
+        prog += [(RBEGIN, 0, 0), (REND, 0, 0, False)]  # first part of tile 0
+        for t in range(n_k):
+            s = t % 2
+            prog += [(RBEGIN, s, t), (REND, s, t)]  # second part of tile t
+            refill = [(ISSUE, s, t + 2, a), (ISSUE, s, t + 2, b)]
+            if refill_before_war:
+                prog += refill
+            if not skip_war:
+                prog.append((BARRIER, nb)); nb += 1
+            if not refill_before_war:
+                prog += refill
+            if not skip_wait:
+                prog.append((WAITLOADS, t + 1))
+            if not skip_raw:
+                prog.append((BARRIER, nb)); nb += 1
+            prog += [(RBEGIN, (t + 1) % 2, t + 1), (REND, (t + 1) % 2, t + 1, False)]  # first part of tile t+1
+        prog.append((WAITLOADS, 10 ** 9))
         progs.append(prog)
     return progs, 2 * W
 
@@ -326,11 +372,13 @@ class _Explorer:
                 self.flag("raw", f"read of tile {t} from slot {s} holding {tags[s]}")
             reading = _set1(reading, s, reading[s] | {w})
         elif k == REND:
-            _, s, t = ins
+            s, t = ins[1], ins[2]
             if t is not None and (any(x != t for x in tags[s]) or any(x is not None for x in writing[s])):
                 self.flag("raw", f"slot {s} changed while tile {t} was read")
             reading = _set1(reading, s, reading[s] - {w})
-            if t is not None:  # a read of data that is never used is no tile read
+            # a read of data that is never used, or the first part of a tile
+            # read in two parts, is no tile read
+            if t is not None and (len(ins) < 4 or ins[3]):
                 log = _set1(log, w, log[w] + (t,))
         elif k == ISSUE:
             _, s, t, share = ins

@@ -241,3 +241,50 @@ def test_kernel_whole_tile_producer_matches_the_model():
     assert loop < wait < load < landed < publish
     assert "constexpr int FP = kWholeTiles ? 1 : P;" in src
     assert "constexpr bool kWholeTiles = !SPLIT && Loader::INSTR < 64;" in src
+
+
+# ------------------------------------------- single schedule, split barriers
+
+@pytest.mark.parametrize("n_k", [0, 1, 2, 3, 5])
+@pytest.mark.parametrize("W", [2, 3])
+def test_split_sync_schedule_safe_in_every_interleaving(n_k, W):
+    # the two-slot ring of the large tile with a WAR and a RAW barrier per tile
+    r = check_swap(2, n_k, W, split_sync=True)
+    assert r.ok, r.example
+    assert r.states > 0
+
+
+@pytest.mark.parametrize("n_k,W", [(12, 2), (9, 4)])
+def test_split_sync_schedule_safe_on_random_interleavings(n_k, W):
+    # W = 4: the kernel's own wave count
+    r = check_swap(2, n_k, W, split_sync=True, exhaustive=False, walks=250, seed=n_k)
+    assert r.ok, r.example
+
+
+@pytest.mark.parametrize("fault", ["skip_barrier", "skip_raw_barrier", "skip_wait", "refill_before_barrier"])
+def test_split_sync_mistakes_are_caught(fault):
+    # skip_barrier drops the WAR barrier: a refill lands while another wave
+    # still reads the tile's second part; the RAW barrier or the wait before
+    # it dropped: a wave reads a tile another wave's loads have not filled
+    r = check_swap(2, 3, 2, split_sync=True, stop_at_first=True, **{fault: True})
+    assert r.raw or r.war, r.example
+
+
+def test_kernel_split_sync_wait_constants_match_the_model():
+    # The two-barrier kernel waits with vmcnt(PER) in the prologue and before
+    # each RAW barrier: one tile's loads (2 issues in the model) may still be
+    # in flight, and every issue of an earlier tile comes before them.
+    for n_k in (1, 2, 5, 9):
+        prog = swap_programs(2, n_k, 1, split_sync=True)[0][0]
+        waits = [i for i, ins in enumerate(prog) if ins[0] == WAITLOADS and ins[1] < 10 ** 9]
+        assert len(waits) == n_k + 1
+        for i in waits:
+            u = prog[i][1]
+            issues = [ins for ins in prog[:i] if ins[0] == ISSUE]
+            later = [ins for ins in issues if ins[2] > u]
+            assert len(later) == 2, (n_k, u)
+            first_later = next(k for k, ins in enumerate(issues) if ins[2] > u)
+            assert all(ins[2] > u for ins in issues[first_later:])
+    src = open(KERNELS).read()
+    assert "wait_vmcnt<PER>();  // tile 0 landed" in src
+    assert "wait_vmcnt<PER>();  // still in flight: the 16 loads of tile t+2" in src
