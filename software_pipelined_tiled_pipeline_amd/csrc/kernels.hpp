@@ -429,6 +429,21 @@ struct NtGeom {
 // step.  A WAR barrier at the first point and a RAW barrier at the second
 // give the refill about three steps, from half a step after its first load
 // to one and a half after its last.
+//
+// SplitSyncPlacement<NM> places the work of a tile's two k32 steps among
+// their NM MFMAs each (see WaveTile::sched_step).  First step: the reads of
+// the second step's fragments, one every REA MFMAs from MFMA RA0 on; the
+// WAR barrier before MFMA WAR; NLA refill loads, one every LEA MFMAs from
+// LA0 on.  Second step: the other NLB refill loads, one every LEB MFMAs
+// from LB0 on; the RAW barrier before MFMA RAW; the reads of the next
+// tile's first-step fragments, one every REB MFMAs from RB0 on.
+template <int NM>
+struct SplitSyncPlacement;
+template <>
+struct SplitSyncPlacement<64> {  // one wave per SIMD, 128 x 128 blocks
+  static constexpr int RA0 = 1, REA = 2, WAR = 40, LA0 = 42, LEA = 4, NLA = 6;
+  static constexpr int LB0 = 2, LEB = 4, NLB = 10, RAW = 44, RB0 = 45, REB = 1;
+};
 template <class G, class Loader, class W>
 constexpr bool kSplitSync = G::P == 0 && G::S == 2 && Loader::DIRECT && W::NK == 2 && W::TM * W::TN == 64;
 
@@ -495,7 +510,8 @@ __global__ void __launch_bounds__(G::THREADS, G::OCC)
     // loads read zeros into slots that are not read again, and the last
     // reads are never used): one code path keeps the accumulators in place.
     constexpr int PER = G::PER_LOADER;
-    static_assert(PER == 16, "the load placement below assumes 16 loads per wave and tile");
+    using Pl = SplitSyncPlacement<W::TM * W::TN>;
+    static_assert(PER == Pl::NLA + Pl::NLB, "the placement issues every load of the wave's share");
     typename W::Frags f[2];
     for (int j = 0; j < 2; ++j) ld.template load<PER>(slot_ptr(j), j, first, lane);
     wait_vmcnt<PER>();  // tile 0 landed
@@ -503,17 +519,18 @@ __global__ void __launch_bounds__(G::THREADS, G::OCC)
     if (n_k > 0) W::read_frags(f[0], lane_a(0), lane_b(0), 0, chunk, sw);
     auto war = []() __attribute__((always_inline)) { lds_barrier(); };
     auto raw = []() __attribute__((always_inline)) {
-      wait_vmcnt<PER>();  // still in flight: the 16 loads of tile t+2
+      wait_vmcnt<PER>();  // still in flight: the PER loads of tile t+2
       __builtin_amdgcn_s_barrier();
     };
     const int p1 = ((4 + chunk) ^ sw) * 16, p0 = (chunk ^ sw) * 16;
     for (int t = 0; t < n_k; ++t) {
       const int s = t & 1, s1 = s ^ 1;
       RefillLoads<Loader> refill{ld, slot_ptr(s), t + 2, first};
-      auto refill_rest = [&](int i) __attribute__((always_inline)) { refill(i + 6); };
-      w.template sched_step<1, 2, 16, 42, 4, 6, 40>(
+      auto refill_rest = [&](int i) __attribute__((always_inline)) { refill(i + Pl::NLA); };
+      constexpr int NR = W::TM + W::TN;
+      w.template sched_step<Pl::RA0, Pl::REA, NR, Pl::LA0, Pl::LEA, Pl::NLA, Pl::WAR>(
           f[0], typename W::FragReads{f[1], lane_a(s), lane_b(s), p1}, refill, war);
-      w.template sched_step<45, 1, 16, 2, 4, 10, 44>(
+      w.template sched_step<Pl::RB0, Pl::REB, NR, Pl::LB0, Pl::LEB, Pl::NLB, Pl::RAW>(
           f[1], typename W::FragReads{f[0], lane_a(s1), lane_b(s1), p0}, refill_rest, raw);
     }
   } else {

@@ -287,4 +287,4 @@ def test_kernel_split_sync_wait_constants_match_the_model():
             assert all(ins[2] > u for ins in issues[first_later:])
     src = open(KERNELS).read()
     assert "wait_vmcnt<PER>();  // tile 0 landed" in src
-    assert "wait_vmcnt<PER>();  // still in flight: the 16 loads of tile t+2" in src
+    assert "wait_vmcnt<PER>();  // still in flight: the PER loads of tile t+2" in src
