@@ -343,7 +343,7 @@ struct WaveTile {
 // The 16-byte output stores (here and in WaveTile::store_direct) are
 // non-temporal: the output is not read again by the kernel, and the tiles
 // resident on one XCD at a time write as much output as its L2 holds (32
-// tiles of 256 x 256 f16 = 4 MiB), which with ordinary stores pushes the
+// tiles of 256 x 256 f16 = 4 MiB), which with ordinary stores can push the
 // lhs and rhs panels of the next tiles out of L2.  Measured: f16 8192^3
 // single schedule S = 2 +3-6 %, producer/consumer unchanged, 4096^3 up to
 // +1 %.  K-split partial sums keep ordinary stores (reduce_splits reads them
