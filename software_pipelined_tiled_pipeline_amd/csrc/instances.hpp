@@ -13,9 +13,11 @@ template <int S>
 using SwapGeom = NtGeom<256, 256, (S <= 2 ? 64 : 32), S, 2, 2, 0>;
 
 // Producer/consumer, large tile: 256 x 256 output tile, eight consumer waves
-// of 128 x 64 (two per SIMD) and four producer waves (one per SIMD), so
-// every wave is capped at 168 registers and a consumer holds one fragment
-// set.  K tile 64 (64 KiB slots) for one or two slots, 32 (32 KiB slots) for
+// of 128 x 64 (two per SIMD) and two producer waves, so two SIMDs hold three
+// waves, every wave is capped at 168 registers and a consumer holds one
+// fragment set.  (Four producers, one per SIMD, cap the registers the same
+// way and measured 0.2-1.2 % slower at every stage count at 8192^3 and at
+// 4096^3: fewer waves compete for the issue slots of the SIMDs.)  K tile 64 (64 KiB slots) for one or two slots, 32 (32 KiB slots) for
 // three or four, so that the ring and the output staging tile fit in 160 KiB
 // of LDS.  (A 256 x 128 tile with four consumers and four producers, one of
 // each per SIMD, gives each wave 256 registers and the consumers two
@@ -23,7 +25,7 @@ using SwapGeom = NtGeom<256, 256, (S <= 2 ? 64 : 32), S, 2, 2, 0>;
 // SIMD idles it at every credit wait, and the narrower tile reads a third
 // more from L2 per flop.)
 template <int S>
-using WsGeom = NtGeom<256, 256, (S <= 2 ? 64 : 32), S, 2, 4, 4>;
+using WsGeom = NtGeom<256, 256, (S <= 2 ? 64 : 32), S, 2, 4, 2>;
 
 // Small tile, for products with too few 256 x 256 tiles to fill the chip
 // (and, with a K split, for skinny ones): 128 x 128 output tile, K tile 64

@@ -46,9 +46,9 @@ def test_ws_protocol_safe_in_every_interleaving(S, n_k, P, C):
     assert r.ok, r.example
 
 
-@pytest.mark.parametrize("S,n_k,P,C", [(4, 16, 4, 8), (2, 20, 4, 8), (3, 12, 2, 4), (1, 8, 4, 8)])
+@pytest.mark.parametrize("S,n_k,P,C", [(4, 16, 2, 8), (2, 20, 2, 8), (3, 12, 2, 4), (1, 8, 2, 8), (4, 16, 4, 8)])
 def test_ws_protocol_safe_on_random_interleavings(S, n_k, P, C):
-    # the kernels' own role counts: 4 producers and 8 consumers (256 x 256
+    # the kernels' own role counts: 2 producers and 8 consumers (256 x 256
     # tiles), 2 and 4 (128 x 128 tiles)
     r = check_ws(S, n_k, P, C, exhaustive=False, walks=200, seed=S + n_k)
     assert r.ok, r.example
@@ -206,10 +206,11 @@ def test_ws_whole_tiles_safe_in_every_interleaving(S, n_k, P, C):
     assert r.ok, r.example
 
 
-@pytest.mark.parametrize("S,n_k,P,C", [(4, 16, 4, 8), (3, 12, 4, 8), (4, 9, 2, 4), (3, 10, 2, 4), (1, 8, 4, 8)])
+@pytest.mark.parametrize("S,n_k,P,C", [(4, 16, 2, 8), (3, 12, 2, 8), (4, 9, 2, 4), (3, 10, 2, 4), (1, 8, 2, 8), (4, 16, 4, 8),
+                                       (3, 12, 4, 8)])
 def test_ws_whole_tiles_safe_on_random_interleavings(S, n_k, P, C):
-    # the kernels' role counts (4 producers / 8 consumers, 2 / 4), with more
-    # producers than slots as well (S = 3, 1)
+    # the kernels' role counts (2 producers / 8 consumers, 2 / 4), with more
+    # producers than slots as well (S = 1 with two, S = 3 with four)
     r = check_ws(S, n_k, P, C, whole_tiles=True, exhaustive=False, walks=200, seed=S * 7 + n_k)
     assert r.ok, r.example
     r = check_ws(S, n_k, P, C, whole_tiles=True, read_after_last=True, exhaustive=False, walks=100, seed=n_k)
