@@ -427,8 +427,8 @@ struct NtGeom {
 // tile t's last fragments have been read (halfway through its first step),
 // and tile t+2 is first read only in the second half of tile t+1's last
 // step.  A WAR barrier at the first point and a RAW barrier at the second
-// give the refill about three steps, from half a step after its first load
-// to one and a half after its last.
+// give each refill load between two and three steps to land (between one
+// and two with the single barrier).
 //
 // SplitSyncPlacement<NM> places the work of a tile's two k32 steps among
 // their NM MFMAs each (see WaveTile::sched_step).  First step: the reads of
