@@ -601,3 +601,24 @@ def test_ws_credit_jitter_keeps_bits(pg, case):
                 assert np.array_equal(got, want), f"S={S} jitter seed {seed:#x} changed the bits"
             assert pg.pgemm_debug_status() == 0
     check_whole(fmt, A, B, {"jittered": got})
+
+
+# ------------------------------------------- single schedule, split barriers
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(520, 300, 4160), (257, 511, 8200), (300, 260, 64 * 41 + 40), (256, 256, 128)])
+def test_split_barrier_schedule_long_and_ragged_k(pg, fmt, M, N, K):
+    """The 256 x 256 single schedule at S = 2 (separate WAR and RAW barriers
+    per K tile): long K with an odd and an even number of K tiles, a K tail
+    inside the last tile, ragged M and N, compared with the oracle element
+    by element, and bit-identical to S = 1 (same k order, one barrier)."""
+    A, B = inputs.make_operands(fmt + "_nt", M, N, K, 700 + M + K)
+    ref, mag = oracle.gemm_nt(fmt, A, B)
+    dA, dB = dev_half(A, fmt), dev_half(B, fmt)
+    with tiling(pg, 256, 0):
+        assert pg.pgemm_query("nt_swap", 2, M, N, K)["block_m"] == 256
+        got = run_nt(pg, fmt, "swap", A, B, 2, dA, dB)
+        one = run_nt(pg, fmt, "swap", A, B, 1, dA, dB)
+    assert_within_bound(fmt, got, ref, mag, f"{fmt} {M}x{N}x{K} swap S=2, 256 x 256")
+    assert np.array_equal(got, one), "S = 2 and S = 1 differ"
